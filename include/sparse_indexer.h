@@ -1,0 +1,233 @@
+/*
+ * sparse_indexer.h - C ABI of the MI355X (gfx950) sparse-attention indexer
+ * hot path.
+ *
+ * Operations, each defined by the page cited at its declaration:
+ *   idx_score_topk       lightning-indexer score + per-query top-K
+ *   dosa_prune_topk      the same top-K through DoSA's certified prune
+ *   kvwitness_merge      segment-witness covering merge, in place
+ *   block_sparse_select  MiniMax-M3 block-sparse block selection
+ *
+ * Conventions shared by every call:
+ *  - Tensor arguments are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or synchronises; scratch space is passed in as
+ *    `workspace` whose size comes from the matching *_workspace() query
+ *    (a pure host function).  Passing more workspace than asked is fine.
+ *  - Every call is asynchronous on the caller's `stream`.
+ *  - Every argument the host can check is checked before any launch; a
+ *    refused call writes nothing.  Device-side launch failures come back as
+ *    SI_ERR_DEVICE.  No call keeps state between calls; calls are safe from
+ *    several threads on different streams.
+ *  - Values the host cannot see without a sync (lengths, offsets and
+ *    positions held in device memory) are clamped on the device so that no
+ *    kernel ever reads or writes out of bounds; out-of-contract values then
+ *    give defined but meaningless results.  Inputs are assumed finite.
+ *  - Index outputs are row-relative int32, padded with -1.
+ *  - Ordering: "top-K" always means the first min(K, n) items under the
+ *    total order (score descending, index ascending), -0 == +0; this one
+ *    order makes tied ids reproducible everywhere.
+ */
+#ifndef SPARSE_INDEXER_H
+#define SPARSE_INDEXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SI_OK = 0,
+  SI_ERR_INVALID_ARGUMENT = 1,
+  /* "Segment Witnesses" page, Refusals: RowsMismatch - the context lengths
+   * do not cover every row (here: context_lens is NULL while rows > 0). */
+  SI_ERR_ROWS_MISMATCH = 2,
+  /* same table: SegmentsOutOfRange - more than 64 segments at the merge */
+  SI_ERR_SEGMENTS_OUT_OF_RANGE = 3,
+  /* same table: LearnedKeepOutOfRange - the retained prefix is wider than the row */
+  SI_ERR_LEARNED_KEEP_OUT_OF_RANGE = 4,
+  SI_ERR_UNSUPPORTED_DTYPE = 5,
+  SI_ERR_WORKSPACE_TOO_SMALL = 6,
+  SI_ERR_DEVICE = 7
+} si_status;
+
+typedef enum { SI_F32 = 0, SI_BF16 = 1, SI_FP8_E4M3FN = 2 } si_dtype;
+
+/* Largest number of witness segments: occupancy travels as one 64-bit mask
+ * ("Segment Witnesses" page, Refusals). */
+#define SI_MAX_TOPOLOGY_SEGMENTS 64
+/* MiniMax-M3's KV block: 128 tokens, also the KV page size (ferrox_core
+ * block_sparse.rs, module docs "The block size is an ABI"). */
+#define SI_MINIMAX_BLOCK_SIZE 128
+
+/* ------------------------------------------------------------------------ *
+ * idx_score_topk
+ *
+ * DoSA reading notes (notes.kuangjux.top), section 3: the indexer score of
+ * key k for a query is  s(k) = sum_h w_h * max(q_h . k, 0)  - all query heads
+ * share one index key, weights are signed.  Section 1: the indexer scores
+ * every visible key and keeps the top-K.
+ *
+ *  q       [n_q, H, D], q_dtype SI_F32 or SI_BF16, row-major.
+ *  k       [n_k, D], k_dtype SI_F32, SI_BF16 or SI_FP8_E4M3FN (OCP e4m3fn).
+ *  k_scale [n_k] f32 per-token scale, required iff k is fp8, else ignored.
+ *          The key is k_scale[j] * e4m3fn(k[j, :]); scales must be > 0.
+ *  w       f32; weight of (row r, head h) is w[r * w_row_stride + h];
+ *          w_row_stride 0 shares one [H] weight vector by all rows.
+ *  k_row_offset [n_q] i64 or NULL.  Row r sees keys
+ *          k[off_r + j], j in [0, vis_r), off_r = k_row_offset[r] (0 if NULL),
+ *          vis_r = clamp(vis_len[r], 0, min(max_vis, n_k - off_r)).
+ *          Row-relative index j is what the outputs hold; the query sits at
+ *          j = vis_r - 1 ("Segment Witnesses" page, Coordinates contract).
+ *  vis_len [n_q] i32.
+ *  max_vis host-side upper bound of every vis_r; sizes the workspace.
+ *  topk    K >= 1.
+ *  out_idx [n_q, K] i32: the top-K of row r (order above), then -1 padding.
+ *  out_score [n_q, K] f32 or NULL: their scores, then -inf padding.
+ *  q, k must be 16-byte aligned; float outputs 4-byte aligned.
+ * Errors: INVALID_ARGUMENT (null pointer, size <= 0 where one is required,
+ * D or H beyond the supported range, misalignment), UNSUPPORTED_DTYPE,
+ * WORKSPACE_TOO_SMALL.
+ * ------------------------------------------------------------------------ */
+si_status idx_score_topk(const void* q, si_dtype q_dtype, const void* k, si_dtype k_dtype,
+                         const float* k_scale, const float* w, int64_t w_row_stride,
+                         const int64_t* k_row_offset, const int32_t* vis_len, int32_t n_q,
+                         int32_t H, int32_t D, int64_t n_k, int64_t max_vis, int32_t topk,
+                         int32_t* out_idx, float* out_score, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+size_t idx_score_topk_workspace(int32_t n_q, int32_t H, int32_t D, int64_t max_vis, int32_t topk);
+
+/* ------------------------------------------------------------------------ *
+ * dosa_prune_topk
+ *
+ * DoSA reading notes, section 2: (1) fully score >= K seed keys, take the
+ * K-th highest seed score as a fixed threshold tau and keep the seeds'
+ * top-K; (2) for every other visible key build a safe upper bound U from the
+ * kept heads' exact activations, a single-anchor residual bound for omitted
+ * positive heads (section 3.1) and a ReLU-aggregated lower bound of the
+ * omitted negative heads' deduction (section 3.2), excluding the key iff
+ * U < tau; (3) rescore survivors exactly, drop those below tau, and take the
+ * final top-K over the seeds' top-K plus the kept survivors.  Section 4:
+ * with no prior, 4 evenly spaced representative queries are fully scored and
+ * 12,288 seeds are chosen by occurrence counts in their top-2048 lists;
+ * error states trigger an exact recovery.
+ *
+ * Prefill layout: keys are shared by all rows (no row offsets), q and k are
+ * SI_BF16, w as in idx_score_topk, row r sees keys [0, vis_r).
+ * The result is bit-identical to idx_score_topk on the same device for the
+ * same inputs (idx and scores).
+ *
+ *  params->n_seeds           seeds (>= topk); 12288 on the page.
+ *  params->n_rep_queries     representative rows for the cold prior (>= 1).
+ *  params->rep_topk          top list length per representative row.
+ *  params->kept_heads        heads scored exactly in the bound (<= 16, < H).
+ *  params->neg_active_frac   omitted negative heads whose activation
+ *                            frequency over the seeds is >= this are
+ *                            aggregated; the rest are dropped (safe).
+ *  params->seed_ids          device [n_seeds] strictly increasing key ids
+ *                            visible to every row, or NULL for the cold
+ *                            prior (the hook a prior from earlier queries
+ *                            would use).
+ *  params->survivor_capacity survivors a row may keep (>= 1); a row with
+ *                            more takes the exact unpruned path.
+ *  stats (optional, device pointers, each may be NULL): tau [n_q],
+ *        n_survivors [n_q] (keys passing the bound), fallback [n_q] (1 when
+ *        the row took the exact path).
+ * Rows fall back to the exact path as a whole when fewer than n_seeds keys
+ * are visible to every row.
+ * Errors: as idx_score_topk, plus INVALID_ARGUMENT for params out of range.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t n_seeds;
+  int32_t n_rep_queries;
+  int32_t rep_topk;
+  int32_t kept_heads;
+  float neg_active_frac;
+  const int32_t* seed_ids;
+  int32_t survivor_capacity;
+} si_dosa_params;
+
+typedef struct {
+  float* tau;
+  int32_t* n_survivors;
+  int32_t* fallback;
+} si_dosa_stats;
+
+si_status dosa_prune_topk(const void* q, const void* k, si_dtype dtype, const float* w,
+                          int64_t w_row_stride, const int32_t* vis_len, int32_t n_q, int32_t H,
+                          int32_t D, int64_t n_k, int32_t topk, const si_dosa_params* params,
+                          int32_t* out_idx, float* out_score, const si_dosa_stats* stats,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+size_t dosa_prune_topk_workspace(int32_t n_q, int32_t H, int32_t D, int64_t n_k, int32_t topk,
+                                 const si_dosa_params* params);
+
+/* ------------------------------------------------------------------------ *
+ * kvwitness_merge  (in place)
+ *
+ * "Segment Witnesses" page (teerth.dev, Aether-Lang kvwitness), sections
+ * Object and Implementation rule and contracts.  For row r with context
+ * length L = context_lens[r] and S_eff = min(S, L), segment s < S_eff is
+ * [e_s, e_{s+1}) with e_s = ceil(s L / S_eff); an entry x in [0, L) occupies
+ * floor(x S_eff / L), an entry x >= L occupies min(floor(x S_eff / L), S - 1),
+ * negative entries are padding.  Witnesses e_s of the unoccupied s < S_eff,
+ * in ascending s, overwrite slots keep, keep+1, ... up to
+ * B = min(max_replacements, topk - keep); the rest are dropped.  Occupancy
+ * is read from the whole row before any write.  Rows with L <= 0 are left
+ * unchanged.  The serving entry uses keep = topk - S (saturating) and
+ * max_replacements = S.
+ *
+ *  topk_idx     [rows, topk] i32 device, modified in place.
+ *  context_lens [rows] i32 device.
+ * Check order (a refused call writes nothing): negative rows/topk/keep/
+ * max_replacements -> INVALID_ARGUMENT; context_lens NULL with rows > 0 ->
+ * ROWS_MISMATCH; topk_idx NULL with rows, topk > 0 -> INVALID_ARGUMENT;
+ * num_segments < 0 or > 64 -> SEGMENTS_OUT_OF_RANGE; keep > topk ->
+ * LEARNED_KEEP_OUT_OF_RANGE.  Then num_segments == 0 (the off switch),
+ * B == 0 or rows == 0 return SI_OK without touching anything.
+ * ------------------------------------------------------------------------ */
+si_status kvwitness_merge(int32_t* topk_idx, int32_t rows, int32_t topk,
+                          const int32_t* context_lens, int32_t num_segments, int32_t keep,
+                          int32_t max_replacements, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * block_sparse_select
+ *
+ * ferrox_core block_sparse.rs (docs.rs, ferrox-core 0.14.0), fns
+ * block_sparse_select / select_for_head / dot.  For query i at position
+ * p = query_pos[i]: n_blocks = min(p / block_size + 1, ceil(n_pos /
+ * block_size)) (0 when p < 0).  Per KV head h independently: the first
+ * min(init_blocks, n) and the last min(local_blocks, n) blocks are forced;
+ * budget = max(top_blocks, #forced); if the forced set already fills the
+ * budget or every block, it is the selection; otherwise every other block is
+ * scored by the MAX over its positions [b*bs, min((b+1)*bs, n_pos, p+1)) of
+ * the f32 dot of index_q[i, h] and index_k[pos] - summed in index order,
+ * each product rounded to f32 before it is added, starting from +0 - and
+ * the best budget - #forced by (score desc, block asc) join the forced
+ * ones.  The selection is written ascending.
+ *
+ *  index_q    [n_q, n_kv_heads, D] f32.   index_k [n_pos, D] f32.
+ *  query_pos  [n_q] i64.
+ *  out_blocks [n_q, n_kv_heads, out_width] i32, ascending, then -1.
+ *  out_count  [n_q, n_kv_heads] i32 (may be NULL).
+ *  out_width  >= max(top_blocks, init_blocks + local_blocks).
+ * Errors: INVALID_ARGUMENT (null pointers, block_size <= 0, negative
+ * counts, out_width too small, D out of range), WORKSPACE_TOO_SMALL.
+ * ------------------------------------------------------------------------ */
+si_status block_sparse_select(const float* index_q, const float* index_k,
+                              const int64_t* query_pos, int32_t n_q, int32_t n_kv_heads,
+                              int32_t D, int64_t n_pos, int32_t block_size, int32_t top_blocks,
+                              int32_t init_blocks, int32_t local_blocks, int32_t* out_blocks,
+                              int32_t out_width, int32_t* out_count, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+size_t block_sparse_select_workspace(int32_t n_q, int32_t n_kv_heads, int64_t n_pos,
+                                     int32_t block_size);
+
+const char* si_status_string(si_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSE_INDEXER_H */

@@ -1,0 +1,10 @@
+"""MI355X-native (gfx950) sparse-attention indexer hot path.
+
+The computation lives in libsparse_indexer.so (hand-written HIP, C ABI in
+include/sparse_indexer.h); this package only marshals torch tensors into it.
+"""
+from ._binding import (SparseIndexerError, block_sparse_select, dosa_prune_topk, idx_score_topk,
+                       kvwitness_merge, lib, status_string)
+
+__all__ = ["idx_score_topk", "dosa_prune_topk", "kvwitness_merge", "block_sparse_select",
+           "SparseIndexerError", "lib", "status_string"]

@@ -1,0 +1,140 @@
+// C-ABI entry points: host-side validation (before any HIP call), workspace
+// carving and launches on the caller's stream.  See include/sparse_indexer.h.
+#include <string.h>
+
+#include "si_internal.hpp"
+
+namespace si {
+hipError_t launch_block_select(const float* q, const float* k, const int64_t* qpos, int32_t n_q,
+                               int32_t H, int32_t D, int64_t n_pos, int32_t bs, int32_t top,
+                               int32_t init, int32_t local, int32_t* out, int32_t width,
+                               int32_t* count, float* ws, hipStream_t st);
+
+static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+static inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+// Shapes the generic (non-MFMA) score path can hold.
+static bool generic_shape_ok(int32_t H, int32_t D) {
+  return H >= 1 && H <= 1024 && D >= 1 && (int64_t)H * D <= 8192;
+}
+
+static size_t score_ws_bytes(int32_t n_q, int64_t max_vis) {
+  if (n_q <= 0 || max_vis <= 0) return 0;
+  return align_up((size_t)n_q * (size_t)max_vis * sizeof(float), 256);
+}
+}  // namespace si
+
+using namespace si;
+
+extern "C" {
+
+const char* si_status_string(si_status s) {
+  switch (s) {
+    case SI_OK: return "ok";
+    case SI_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SI_ERR_ROWS_MISMATCH: return "context lengths do not cover every row";
+    case SI_ERR_SEGMENTS_OUT_OF_RANGE: return "num_segments out of range (0..64)";
+    case SI_ERR_LEARNED_KEEP_OUT_OF_RANGE: return "keep exceeds the row width";
+    case SI_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+    case SI_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case SI_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+size_t idx_score_topk_workspace(int32_t n_q, int32_t H, int32_t D, int64_t max_vis, int32_t topk) {
+  (void)H;
+  (void)D;
+  (void)topk;
+  return score_ws_bytes(n_q, max_vis);
+}
+
+si_status idx_score_topk(const void* q, si_dtype q_dtype, const void* k, si_dtype k_dtype,
+                         const float* k_scale, const float* w, int64_t w_row_stride,
+                         const int64_t* k_row_offset, const int32_t* vis_len, int32_t n_q,
+                         int32_t H, int32_t D, int64_t n_k, int64_t max_vis, int32_t topk,
+                         int32_t* out_idx, float* out_score, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (n_q < 0 || H < 1 || D < 1 || n_k < 0 || max_vis < 0 || topk < 1 || topk > kMaxTopk ||
+      w_row_stride < 0)
+    return SI_ERR_INVALID_ARGUMENT;
+  if (q_dtype != SI_F32 && q_dtype != SI_BF16) return SI_ERR_UNSUPPORTED_DTYPE;
+  if (k_dtype != SI_F32 && k_dtype != SI_BF16 && k_dtype != SI_FP8_E4M3FN)
+    return SI_ERR_UNSUPPORTED_DTYPE;
+  if (max_vis > INT32_MAX) return SI_ERR_INVALID_ARGUMENT;  // row-relative ids are int32
+  if (n_q == 0) return SI_OK;
+  if (!q || !k || !w || !vis_len || !out_idx) return SI_ERR_INVALID_ARGUMENT;
+  if (k_dtype == SI_FP8_E4M3FN && !k_scale) return SI_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned4(w) || !aligned4(out_idx) ||
+      (out_score && !aligned4(out_score)))
+    return SI_ERR_INVALID_ARGUMENT;
+  ScoreArgs sa;
+  sa.q = q; sa.q_dtype = q_dtype; sa.k = k; sa.k_dtype = k_dtype; sa.k_scale = k_scale;
+  sa.w = w; sa.w_row_stride = w_row_stride; sa.k_row_offset = k_row_offset; sa.vis_len = vis_len;
+  sa.n_q = n_q; sa.H = H; sa.D = D; sa.n_k = n_k; sa.max_vis = max_vis;
+  sa.scores = nullptr; sa.score_stride = max_vis;
+  if (!score_mfma_supported(sa) && !generic_shape_ok(H, D)) return SI_ERR_INVALID_ARGUMENT;
+  const size_t need = score_ws_bytes(n_q, max_vis);
+  if (need && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return SI_ERR_WORKSPACE_TOO_SMALL;
+  sa.scores = reinterpret_cast<float*>(workspace);
+
+  hipError_t e = launch_score(sa, stream);
+  if (e != hipSuccess) return SI_ERR_DEVICE;
+  TopkArgs ta;
+  ta.scores = sa.scores; ta.stride = max_vis; ta.vis_len = vis_len; ta.k_row_offset = k_row_offset;
+  ta.n_k = n_k; ta.max_vis = max_vis; ta.n_rows = n_q; ta.K = topk; ta.out_idx = out_idx;
+  ta.out_score = out_score; ta.id_map = nullptr;
+  e = launch_topk(ta, stream);
+  return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
+}
+
+si_status kvwitness_merge(int32_t* topk_idx, int32_t rows, int32_t topk,
+                          const int32_t* context_lens, int32_t num_segments, int32_t keep,
+                          int32_t max_replacements, hipStream_t stream) {
+  if (rows < 0 || topk < 0 || keep < 0 || max_replacements < 0) return SI_ERR_INVALID_ARGUMENT;
+  if (rows > 0 && !context_lens) return SI_ERR_ROWS_MISMATCH;
+  if (rows > 0 && topk > 0 && !topk_idx) return SI_ERR_INVALID_ARGUMENT;
+  if (num_segments < 0 || num_segments > SI_MAX_TOPOLOGY_SEGMENTS)
+    return SI_ERR_SEGMENTS_OUT_OF_RANGE;
+  if (keep > topk) return SI_ERR_LEARNED_KEEP_OUT_OF_RANGE;
+  const int32_t B = max_replacements < topk - keep ? max_replacements : topk - keep;
+  if (num_segments == 0 || B == 0 || rows == 0) return SI_OK;
+  if (!aligned4(topk_idx) || !aligned4(context_lens)) return SI_ERR_INVALID_ARGUMENT;
+  hipError_t e = launch_witness(topk_idx, rows, topk, context_lens, num_segments, keep, B, stream);
+  return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
+}
+
+si_status block_sparse_select(const float* index_q, const float* index_k,
+                              const int64_t* query_pos, int32_t n_q, int32_t n_kv_heads,
+                              int32_t D, int64_t n_pos, int32_t block_size, int32_t top_blocks,
+                              int32_t init_blocks, int32_t local_blocks, int32_t* out_blocks,
+                              int32_t out_width, int32_t* out_count, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  if (n_q < 0 || n_kv_heads < 1 || D < 1 || D > 65536 || n_pos < 0 || block_size < 1 ||
+      top_blocks < 0 || init_blocks < 0 || local_blocks < 0)
+    return SI_ERR_INVALID_ARGUMENT;
+  const int64_t need_w = top_blocks > (int64_t)init_blocks + local_blocks
+                             ? top_blocks
+                             : (int64_t)init_blocks + local_blocks;
+  if (out_width < need_w || out_width < 1 || out_width > kMaxTopk) return SI_ERR_INVALID_ARGUMENT;
+  const int64_t max_blocks = (n_pos + block_size - 1) / block_size;
+  if (max_blocks > INT32_MAX) return SI_ERR_INVALID_ARGUMENT;
+  if (n_q == 0) return SI_OK;
+  if (!index_q || (!index_k && n_pos > 0) || !query_pos || !out_blocks)
+    return SI_ERR_INVALID_ARGUMENT;
+  if ((int64_t)n_q * n_kv_heads > INT32_MAX) return SI_ERR_INVALID_ARGUMENT;
+  const int64_t qt = n_kv_heads >= 32 ? 1 : 32 / n_kv_heads;
+  if (((n_q + qt - 1) / qt) * max_blocks > INT32_MAX) return SI_ERR_INVALID_ARGUMENT;
+  const size_t need = block_sparse_select_workspace(n_q, n_kv_heads, n_pos, block_size);
+  if (need && (!workspace || workspace_bytes < need || !aligned4(workspace)))
+    return SI_ERR_WORKSPACE_TOO_SMALL;
+  hipError_t e = launch_block_select(index_q, index_k, query_pos, n_q, n_kv_heads, D, n_pos,
+                                     block_size, top_blocks, init_blocks, local_blocks, out_blocks,
+                                     out_width, out_count, reinterpret_cast<float*>(workspace),
+                                     stream);
+  return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
+}
+
+}  // extern "C"

@@ -1,0 +1,231 @@
+// MiniMax-M3 block-sparse selection (ferrox_core block_sparse.rs:
+// block_sparse_select, select_for_head, dot).
+//
+// Pass 1 (block_max): a block's score for (query, KV head) is the MAX over
+// the block's causally visible positions of the page's f32 dot - products
+// rounded to f32 and added in index order from +0, never fused.  That order
+// is part of the definition, so the dots run on the VALU with contraction
+// off; each lane owns one position and carries RC row accumulators
+// (row = query x head of the workgroup's query tile), the query values are
+// wave-uniform, the block's keys are staged in LDS in 32-wide d chunks.
+// Pass 2 (select): per (query, head), force the init/local blocks, radix
+// select the best budget - #forced of the others by (score desc, block asc),
+// and write the union ascending.
+#include "si_internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace si {
+
+constexpr int kBlkThreads = 128;  // lanes = positions of one block pass
+constexpr int kBlkRows = 32;      // accumulator rows per lane
+constexpr int kBlkDChunk = 32;
+
+__device__ __forceinline__ int64_t n_blocks_of(int64_t pos, int64_t n_pos, int bs) {
+  if (pos < 0) return 0;
+  int64_t nb = pos / bs + 1;
+  int64_t ex = (n_pos + bs - 1) / bs;
+  return nb < ex ? nb : ex;
+}
+
+struct BlockArgs {
+  const float* q;
+  const float* k;
+  const int64_t* qpos;
+  int32_t n_q, H, D;
+  int64_t n_pos;
+  int32_t bs, top, init, local;
+  int32_t* out;
+  int32_t width;
+  int32_t* count;
+  float* bscore;  // [n_q, H, max_blocks]
+  int64_t max_blocks;
+  int32_t qt;     // queries per tile (rows per tile = qt * H)
+};
+
+__global__ __launch_bounds__(kBlkThreads) void block_max(BlockArgs a) {
+  __shared__ float ks[kBlkThreads][kBlkDChunk + 1];
+  __shared__ float red[kBlkThreads / 64][kBlkRows];
+  const int64_t lin = blockIdx.x;
+  const int64_t b = lin % a.max_blocks;
+  const int tile = (int)(lin / a.max_blocks);
+  const int q0 = tile * a.qt;
+  const int rows = a.qt * a.H;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+
+  // furthest position any query of the tile may see in this block
+  int64_t maxpos = -1;
+  for (int i = 0; i < a.qt && q0 + i < a.n_q; ++i) {
+    int64_t p = a.qpos[q0 + i];
+    if (b < n_blocks_of(p, a.n_pos, a.bs) && p > maxpos) maxpos = p;
+  }
+  if (maxpos < 0) return;
+  const int64_t blk_lo = b * a.bs;
+  int64_t blk_hi = blk_lo + a.bs;
+  if (blk_hi > a.n_pos) blk_hi = a.n_pos;
+  if (blk_hi > maxpos + 1) blk_hi = maxpos + 1;
+
+  for (int r0 = 0; r0 < rows; r0 += kBlkRows) {
+    float best[kBlkRows];
+#pragma unroll
+    for (int i = 0; i < kBlkRows; ++i) best[i] = -__builtin_inff();
+    for (int64_t p0 = blk_lo; p0 < blk_hi; p0 += kBlkThreads) {
+      const int64_t p = p0 + t;
+      float acc[kBlkRows];
+#pragma unroll
+      for (int i = 0; i < kBlkRows; ++i) acc[i] = 0.0f;  // +0 start
+      for (int dc = 0; dc < a.D; dc += kBlkDChunk) {
+        const int dn = (a.D - dc) < kBlkDChunk ? (a.D - dc) : kBlkDChunk;
+        __syncthreads();
+        for (int e = t; e < kBlkThreads * kBlkDChunk; e += kBlkThreads) {
+          int pr = e / kBlkDChunk, c = e % kBlkDChunk;
+          int64_t pp = p0 + pr;
+          ks[pr][c] = (pp < blk_hi && c < dn) ? a.k[pp * a.D + dc + c] : 0.0f;
+        }
+        __syncthreads();
+        for (int c = 0; c < dn; ++c) {
+          const float kd = ks[t][c];
+#pragma unroll
+          for (int i = 0; i < kBlkRows; ++i) {
+            const int row = r0 + i;
+            const int qi = row / a.H, h = row - qi * a.H;
+            const int qq = q0 + qi;
+            float qv = 0.0f;
+            if (row < rows && qq < a.n_q) qv = a.q[((int64_t)qq * a.H + h) * a.D + dc + c];
+            const float prod = qv * kd;
+            acc[i] = acc[i] + prod;
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kBlkRows; ++i) {
+        const int row = r0 + i;
+        const int qq = q0 + row / a.H;
+        bool vis = p < blk_hi && row < rows && qq < a.n_q && p <= a.qpos[qq];
+        if (vis && acc[i] > best[i]) best[i] = acc[i];
+      }
+    }
+    // max over the block's positions (exact in any order)
+#pragma unroll
+    for (int i = 0; i < kBlkRows; ++i) {
+      float v = best[i];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+      if (lane == 0) red[wv][i] = v;
+    }
+    __syncthreads();
+    if (t < kBlkRows) {
+      const int row = r0 + t;
+      const int qi = row / a.H, h = row - qi * a.H;
+      const int qq = q0 + qi;
+      if (row < rows && qq < a.n_q && b < n_blocks_of(a.qpos[qq], a.n_pos, a.bs)) {
+        float v = red[0][t];
+        for (int w2 = 1; w2 < kBlkThreads / 64; ++w2) v = __builtin_fmaxf(v, red[w2][t]);
+        a.bscore[((int64_t)qq * a.H + h) * a.max_blocks + b] = v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+constexpr int kSelThreads = 256;
+
+__global__ __launch_bounds__(kSelThreads) void block_select(BlockArgs a) {
+  __shared__ int hist[2048];
+  __shared__ int red[kSelThreads / 64 + 4];
+  __shared__ uint64_t list[kMaxTopk];
+  __shared__ int counter;
+  const int qq = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int64_t n = n_blocks_of(a.qpos[qq], a.n_pos, a.bs);
+  int32_t* out = a.out + (int64_t)blockIdx.x * a.width;
+  const int64_t fi = a.init < n ? a.init : n;
+  const int64_t ls = n - (a.local < n ? a.local : n);  // first local block
+  const int64_t lo_end = fi, hi_beg = ls > fi ? ls : fi;
+  const int64_t nf = lo_end + (n - hi_beg);
+  const int64_t budget = a.top > nf ? a.top : nf;
+  int64_t total;  // blocks written
+  if (threadIdx.x == 0) counter = 0;
+  __syncthreads();
+  if (n == 0) {
+    total = 0;
+  } else if (nf >= budget || nf == n) {
+    for (int64_t i = threadIdx.x; i < nf; i += kSelThreads)
+      out[i] = (int32_t)(i < lo_end ? i : hi_beg + (i - lo_end));
+    total = nf;
+  } else {
+    const int64_t m = hi_beg - lo_end;  // scored blocks [fi, ls)
+    const int64_t take = (budget - nf) < m ? (budget - nf) : m;
+    if (take == m) {
+      for (int64_t i = threadIdx.x; i < n; i += kSelThreads) out[i] = (int32_t)i;
+      total = n;
+    } else {
+      const float* sc = a.bscore + (int64_t)blockIdx.x * a.max_blocks + lo_end;
+      auto load = [&](int64_t i) -> uint32_t { return order_key(sc[i]); };
+      int64_t n_gt;
+      const uint32_t thr = radix_select_kth<kSelThreads>(load, m, take, hist, red, &n_gt);
+      // forced blocks first, then the chosen ones; values are ~block so a
+      // descending sort gives ascending blocks
+      for (int64_t i = threadIdx.x; i < nf; i += kSelThreads) {
+        int64_t blk = i < lo_end ? i : hi_beg + (i - lo_end);
+        list[i] = (uint64_t)(0xFFFFFFFFu - (uint32_t)blk);
+      }
+      for (int64_t i = threadIdx.x; i < m; i += kSelThreads)
+        if (load(i) > thr)
+          list[nf + atomicAdd(&counter, 1)] = (uint64_t)(0xFFFFFFFFu - (uint32_t)(lo_end + i));
+      const int need = (int)(take - n_gt);
+      int taken = 0;
+      for (int64_t base = 0; base < m && taken < need; base += kSelThreads) {
+        int64_t i = base + threadIdx.x;
+        int flag = (i < m && load(i) == thr) ? 1 : 0;
+        int tot;
+        int rank = block_excl_scan<kSelThreads>(flag, red, &tot);
+        if (flag && taken + rank < need)
+          list[nf + n_gt + taken + rank] = (uint64_t)(0xFFFFFFFFu - (uint32_t)(lo_end + i));
+        taken += tot;
+      }
+      total = nf + take;
+      const int P = next_pow2((int)total);
+      for (int i = (int)total + threadIdx.x; i < P; i += kSelThreads) list[i] = 0ull;
+      __syncthreads();
+      bitonic_sort_desc<kSelThreads>(list, P);
+      for (int64_t i = threadIdx.x; i < total; i += kSelThreads)
+        out[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)list[i]);
+    }
+  }
+  for (int64_t i = total + threadIdx.x; i < a.width; i += kSelThreads) out[i] = -1;
+  if (a.count && threadIdx.x == 0) a.count[blockIdx.x] = (int32_t)total;
+}
+
+}  // namespace si
+
+extern "C" size_t block_sparse_select_workspace(int32_t n_q, int32_t n_kv_heads, int64_t n_pos,
+                                                int32_t block_size) {
+  if (n_q <= 0 || n_kv_heads <= 0 || n_pos <= 0 || block_size <= 0) return 0;
+  const int64_t mb = (n_pos + block_size - 1) / block_size;
+  return (size_t)n_q * (size_t)n_kv_heads * (size_t)mb * sizeof(float);
+}
+
+namespace si {
+hipError_t launch_block_select(const float* q, const float* k, const int64_t* qpos, int32_t n_q,
+                               int32_t H, int32_t D, int64_t n_pos, int32_t bs, int32_t top,
+                               int32_t init, int32_t local, int32_t* out, int32_t width,
+                               int32_t* count, float* ws, hipStream_t st) {
+  BlockArgs a;
+  a.q = q; a.k = k; a.qpos = qpos; a.n_q = n_q; a.H = H; a.D = D; a.n_pos = n_pos;
+  a.bs = bs; a.top = top; a.init = init; a.local = local; a.out = out; a.width = width;
+  a.count = count; a.bscore = ws;
+  a.max_blocks = (n_pos + bs - 1) / bs;
+  a.qt = H >= kBlkRows ? 1 : kBlkRows / H;
+  if (n_q == 0) return hipSuccess;
+  const int64_t tiles = (n_q + a.qt - 1) / a.qt;
+  if (tiles * a.max_blocks > 0) {
+    hipLaunchKernelGGL(block_max, dim3((unsigned)(tiles * a.max_blocks)), dim3(kBlkThreads), 0,
+                       st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(block_select, dim3((unsigned)((int64_t)n_q * H)), dim3(kSelThreads), 0, st,
+                     a);
+  return hipGetLastError();
+}
+}  // namespace si

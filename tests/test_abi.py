@@ -1,0 +1,174 @@
+"""The C-ABI library loads, exports every function include/*.h declares, and
+refuses malformed calls on the host before any HIP call, leaving every
+buffer untouched.  Runs without a GPU: the refusals never reach the device,
+so host buffers are safe to pass."""
+import ctypes as C
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, INVALID, ROWS_MISMATCH, SEGS, KEEP, DTYPE, WS, DEVICE = range(8)
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+([a-z_][a-z0-9_]*)\s*\(",
+                             text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    import sparse_attention_indexer_02_amd as si
+    return si.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert {"idx_score_topk", "dosa_prune_topk", "kvwitness_merge", "block_sparse_select",
+            "idx_score_topk_workspace", "dosa_prune_topk_workspace",
+            "block_sparse_select_workspace", "si_status_string"} <= names
+    missing = [n for n in sorted(names) if getattr(L, n, None) is None]
+    assert not missing, f"declared but not exported: {missing}"
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert L.si_status_string(s)
+    assert b"64" in L.si_status_string(SEGS)
+
+
+def _p(a):
+    return a.ctypes.data
+
+
+def test_witness_refusals_touch_nothing(L):
+    rows = np.arange(32, dtype=np.int32).reshape(4, 8)
+    lens = np.full(4, 20, np.int32)
+    before = rows.copy()
+    cases = [
+        ((_p(rows), -1, 8, _p(lens), 4, 4, 4), INVALID),
+        ((_p(rows), 4, -8, _p(lens), 4, 4, 4), INVALID),
+        ((_p(rows), 4, 8, _p(lens), 4, -1, 4), INVALID),
+        ((_p(rows), 4, 8, _p(lens), 4, 4, -1), INVALID),
+        ((_p(rows), 4, 8, None, 4, 4, 4), ROWS_MISMATCH),
+        ((None, 4, 8, _p(lens), 4, 4, 4), INVALID),
+        ((_p(rows), 4, 8, _p(lens), 65, 4, 4), SEGS),
+        ((_p(rows), 4, 8, _p(lens), -1, 4, 4), SEGS),
+        ((_p(rows), 4, 8, _p(lens), 4, 9, 4), KEEP),
+        # identities: the off switch, B = 0, zero rows - OK and no launch
+        ((_p(rows), 4, 8, _p(lens), 0, 4, 4), OK),
+        ((_p(rows), 4, 8, _p(lens), 4, 8, 4), OK),
+        ((_p(rows), 4, 8, _p(lens), 4, 4, 0), OK),
+        ((_p(rows), 0, 8, _p(lens), 4, 4, 4), OK),
+    ]
+    for args, want in cases:
+        assert L.kvwitness_merge(*args, None) == want, args
+        np.testing.assert_array_equal(rows, before)
+
+
+def test_idx_score_topk_refusals(L):
+    n_q, H, D, n_k, K = 4, 64, 128, 100, 16
+    q = np.zeros(n_q * H * D + 8, np.uint16)
+    k = np.zeros(n_k * D + 8, np.uint16)
+    w = np.zeros(n_q * H, np.float32)
+    vis = np.full(n_q, n_k, np.int32)
+    out = np.full(n_q * K, 7, np.int32)
+    outs = np.full(n_q * K, 7.0, np.float32)
+    ws_need = L.idx_score_topk_workspace(n_q, H, D, n_k, K)
+    assert ws_need >= n_q * n_k * 4
+    ws = np.zeros(16, np.uint8)
+
+    def al(a):  # 16-byte aligned view start
+        return a.ctypes.data + (-a.ctypes.data) % 16
+
+    base = dict(q=al(q), qd=1, k=al(k), kd=1, ks=None, w=_p(w), ws_=H, off=None, vis=_p(vis),
+                n_q=n_q, H=H, D=D, n_k=n_k, mv=n_k, K=K, oi=_p(out), os=_p(outs), wsp=_p(ws),
+                wsb=16)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.idx_score_topk(a["q"], a["qd"], a["k"], a["kd"], a["ks"], a["w"], a["ws_"],
+                                a["off"], a["vis"], a["n_q"], a["H"], a["D"], a["n_k"], a["mv"],
+                                a["K"], a["oi"], a["os"], a["wsp"], a["wsb"], None)
+
+    assert call(K=0) == INVALID
+    assert call(K=4097) == INVALID
+    assert call(n_q=-1) == INVALID
+    assert call(ws_=-1) == INVALID
+    assert call(qd=2) == DTYPE
+    assert call(kd=3) == DTYPE
+    assert call(q=None) == INVALID
+    assert call(vis=None) == INVALID
+    assert call(kd=2) == INVALID  # fp8 keys need scales
+    assert call(q=al(q) + 2) == INVALID  # misaligned
+    assert call(qd=1, H=65) == INVALID  # bf16 beyond the MFMA head range and generic LDS
+    assert call() == WS  # workspace too small
+    assert call(n_q=0) == OK
+    np.testing.assert_array_equal(out, 7)
+    np.testing.assert_array_equal(outs, 7.0)
+
+
+def test_block_select_refusals(L):
+    q = np.zeros(64, np.float32)
+    k = np.zeros(64, np.float32)
+    pos = np.zeros(2, np.int64)
+    out = np.full(2 * 2 * 4, 5, np.int32)
+    cnt = np.full(4, 5, np.int32)
+    ws = np.zeros(4, np.uint8)
+
+    def call(n_q=2, H=2, D=4, n_pos=16, bs=4, top=3, init=1, local=1, width=4, wsb=4,
+             qp=_p(q)):
+        return L.block_sparse_select(qp, _p(k), _p(pos), n_q, H, D, n_pos, bs, top, init, local,
+                                     _p(out), width, _p(cnt), _p(ws), wsb, None)
+
+    assert call(bs=0) == INVALID
+    assert call(top=-1) == INVALID
+    assert call(width=2) == INVALID  # narrower than top_blocks
+    assert call(init=3, local=3, width=5) == INVALID  # narrower than init + local
+    assert call(width=5000, top=5000) == INVALID
+    assert call(qp=None) == INVALID
+    assert call() == WS
+    assert call(n_q=0) == OK
+    assert L.block_sparse_select_workspace(2, 2, 16, 4) == 2 * 2 * 4 * 4
+    np.testing.assert_array_equal(out, 5)
+    np.testing.assert_array_equal(cnt, 5)
+
+
+def test_dosa_refusals(L):
+    from sparse_attention_indexer_02_amd._binding import DosaParams
+    n_q, H, D, n_k, K = 4, 32, 128, 64, 8
+    q = np.zeros(n_q * H * D + 8, np.uint16)
+    k = np.zeros(n_k * D + 8, np.uint16)
+    w = np.zeros(n_q * H, np.float32)
+    vis = np.full(n_q, n_k, np.int32)
+    out = np.full(n_q * K, 3, np.int32)
+    ws = np.zeros(16, np.uint8)
+
+    def al(a):
+        return a.ctypes.data + (-a.ctypes.data) % 16
+
+    def call(p, dtype=1, topk=K, wsb=16, qq=al(q)):
+        return L.dosa_prune_topk(qq, al(k), dtype, _p(w), H, _p(vis), n_q, H, D, n_k, topk,
+                                 C.byref(p), _p(out), None, None, _p(ws), wsb, None)
+
+    good = DosaParams(16, 4, 8, 8, 0.5, None, 64)
+    assert call(DosaParams(4, 4, 8, 8, 0.5, None, 64)) == INVALID  # n_seeds < topk
+    assert call(DosaParams(16, 0, 8, 8, 0.5, None, 64)) == INVALID  # no representative rows
+    assert call(DosaParams(16, 4, 8, 17, 0.5, None, 64)) == INVALID  # kept_heads > 16
+    assert call(DosaParams(16, 4, 8, 8, 0.5, None, 0)) == INVALID  # capacity
+    assert call(good, dtype=0) == DTYPE
+    assert call(good, qq=None) == INVALID
+    assert call(good) == WS
+    assert L.dosa_prune_topk(al(q), al(k), 1, _p(w), H, _p(vis), 0, H, D, n_k, K, C.byref(good),
+                             _p(out), None, None, _p(ws), 16, None) == OK
+    np.testing.assert_array_equal(out, 3)
