@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse-attention indexer hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload prefill|decode|dosa|dosa_structured|block]
+
+Default workload: the DSA-style causal prefill chunk, 8192 queries x 8192
+keys, H=64, D=128, bf16, K=2048, then the segment-witness merge (S=16,
+serving keep/budget).  One step = score rows (MFMA kernel) -> top-K ids
+(radix-select kernel) -> witness merge, all on the current HIP stream with
+inputs resident in HBM.  value = visible query-key pairs per second of the
+whole step.  Per-kernel times come from HIP events recorded on that stream
+around each stage.
+
+Prints ONE JSON line.  With --gpus N > 1 it exits: this build measures one
+GPU (row sharding across GPUs is described in the design notes).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer query·key pairs scored+top-K'd /sec at H64 D128 K2048; % MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one non-packed fp32 op per lane-cycle
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def counters_for(kernel_file, workload):
+    """HBM traffic per launch measured with rocprofv3 PMC counters, if the
+    summary in profiles/ was taken on the kernel source as it is now."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        ent = data[workload]
+        src = open(os.path.join(ROOT, "sparse_attention_indexer_02_amd", "csrc", kernel_file),
+                   "rb").read()
+        if ent["source_sha256"] != hashlib.sha256(src).hexdigest():
+            return None
+        return ent["hbm_bytes_per_launch"]
+    except (KeyError, ValueError, OSError):
+        return None
+
+
+def to_device(cfg):
+    """Synthetic host arrays -> torch device tensors (bf16 travels as int16 bits)."""
+    import numpy as np
+    import torch
+
+    def bits(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(dt).cuda()
+
+    q = bits(cfg["q"], torch.bfloat16) if cfg["q_dtype"] == 1 else torch.from_numpy(cfg["q"]).cuda()
+    k = bits(cfg["k"], torch.bfloat16) if cfg["k_dtype"] == 1 else \
+        torch.from_numpy(np.ascontiguousarray(cfg["k"])).cuda()
+    opt = lambda a, dt: None if a is None else torch.from_numpy(np.ascontiguousarray(a, dt)).cuda()
+    return dict(q=q, k=k, k_scale=opt(cfg.get("k_scale"), np.float32),
+                w=opt(cfg["w"], np.float32), vis_len=opt(cfg["vis_len"], np.int32),
+                k_row_offset=opt(cfg.get("k_row_offset"), np.int64))
+
+
+def timed_steps(stages, steps, warmup):
+    """Run warmup + steps; return wall ms/step and mean ms per stage (events)."""
+    import torch
+    for _ in range(warmup):
+        for _, fn in stages:
+            fn()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        evs[s][0].record()
+        for i, (_, fn) in enumerate(stages):
+            fn()
+            evs[s][i + 1].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    per = {}
+    for i, (name, _) in enumerate(stages):
+        per[name] = sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)) / steps
+    return wall_ms, per
+
+
+def cpu_baseline_rows(cfg, seconds, witness=None):
+    """The oracle, as it stands, on evenly spaced rows of the workload: grows
+    the sample until it has run about `seconds` (bounded)."""
+    import numpy as np
+
+    import oracle
+    kp = oracle.problem(cfg)
+    n = 16
+    elapsed, pairs, rows = 0.0, 0, []
+    while True:
+        rows = np.unique(np.linspace(0, cfg["n_q"] - 1, min(n, cfg["n_q"])).astype(np.int32))
+        t0 = time.perf_counter()
+        idx, _ = oracle.idx_score_topk_rows(kp, rows)
+        if witness is not None:
+            oracle.kvwitness_merge(idx, cfg["vis_len"][rows], witness["S"], witness["keep"],
+                                   witness["max_rep"])
+        elapsed = time.perf_counter() - t0
+        pairs = int(sum(oracle.visible(kp, int(r)) for r in rows))
+        if elapsed >= seconds * 0.5 or len(rows) >= cfg["n_q"]:
+            break
+        n = int(n * min(8.0, max(2.0, seconds / max(elapsed, 1e-3))))
+    return dict(value=pairs / elapsed, unit="pairs/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{len(rows)} evenly spaced rows of the {cfg['n_q']}-row workload "
+                       f"({pairs} pairs, {elapsed:.1f} s: score + top-K"
+                       f"{' + witness' if witness else ''})")
+
+
+def bench_indexer(args, cfg, workload):
+    import numpy as np
+    import torch
+
+    import sparse_attention_indexer_02_amd as si
+    d = to_device(cfg)
+    n_q, H, D, K, mv = cfg["n_q"], cfg["H"], cfg["D"], cfg["topk"], cfg["max_vis"]
+    dev = d["q"].device
+    scores = torch.empty((n_q, mv), dtype=torch.float32, device=dev)
+    out_idx = torch.empty((n_q, K), dtype=torch.int32, device=dev)
+    wit = cfg["witness"]
+    pairs = int(np.minimum(np.maximum(cfg["vis_len"].astype(np.int64), 0), mv).sum())
+
+    def score():
+        si.idx_score(d["q"], d["k"], d["w"], d["vis_len"], k_scale=d["k_scale"],
+                     k_row_offset=d["k_row_offset"], max_vis=mv, out_scores=scores)
+
+    def topk():
+        si.rows_topk(scores, d["vis_len"], K, k_row_offset=d["k_row_offset"], n_k=cfg["n_k"],
+                     max_vis=mv, out_idx=out_idx, want_scores=False)
+
+    def witness():
+        si.kvwitness_merge(out_idx, d["vis_len"], wit["S"], wit["keep"], wit["max_rep"])
+
+    stages = [("score", score), ("topk", topk), ("witness", witness)]
+    log(f"{workload}: {pairs} visible pairs, warmup {args.warmup}, steps {args.steps}")
+    wall_ms, per = timed_steps(stages, args.steps, args.warmup)
+
+    flops = pairs * 2.0 * H * D
+    kbytes = cfg["k"].nbytes + (cfg["k_scale"].nbytes if cfg["k_scale"] is not None else 0)
+    score_bytes = cfg["q"].nbytes + kbytes + cfg["w"].nbytes + pairs * 4
+    topk_bytes = pairs * 4 + n_q * K * 4
+    B = min(wit["max_rep"], K - wit["keep"])
+    wit_bytes = n_q * K * 4 + n_q * 4 + n_q * B * 4
+    kern = {
+        "score": dict(ms=per["score"], tflops=flops / per["score"] / 1e9,
+                      gbs=score_bytes / per["score"] / 1e6, algo_flops=flops,
+                      algo_bytes=score_bytes),
+        "topk": dict(ms=per["topk"], gbs=topk_bytes / per["topk"] / 1e6, algo_bytes=topk_bytes),
+        "witness": dict(ms=per["witness"], gbs=wit_bytes / per["witness"] / 1e6,
+                        algo_bytes=wit_bytes),
+    }
+    for kk in kern.values():
+        kk["hbm_frac"] = kk["gbs"] / PEAK_HBM_GBS
+    kern["score"]["mfma_frac"] = kern["score"]["tflops"] / PEAK_BF16_TFLOPS
+
+    if workload == "decode":
+        # per-row keys: every key byte is read once; HBM-bound
+        ach = score_bytes / per["score"] / 1e6
+        roof = dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=ach / PEAK_HBM_GBS, traffic=counters_for("score.hip", workload),
+                    kernel="score_mfma_rows")
+    else:
+        ach = kern["score"]["tflops"]
+        roof = dict(bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=ach / PEAK_BF16_TFLOPS, traffic=counters_for("score.hip", workload),
+                    kernel="score_mfma_shared")
+    step_ms = per["score"] + per["topk"] + per["witness"]
+    out = dict(metric=METRIC, value=pairs / (wall_ms / 1e3), unit="pairs/s", n_gpus=1,
+               steps=args.steps, warmup=args.warmup, ms_per_step=wall_ms, higher_is_better=True,
+               scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+               config=dict(workload=workload_name(cfg, workload), n_q=n_q, H=H, D=D,
+                           n_keys=cfg["n_k"], topk=K, witness_segments=wit["S"],
+                           key_dtype={0: "f32", 1: "bf16", 2: "fp8_e4m3fn"}[cfg["k_dtype"]],
+                           pairs_per_step=pairs),
+               roofline=roof, kernels=kern, event_ms_per_step=step_ms)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline_rows(cfg, args.cpu_seconds, wit)
+    return out
+
+
+def workload_name(cfg, workload):
+    if workload == "prefill":
+        return (f"causal prefill {cfg['n_q']}x{cfg['n_k']} H{cfg['H']} D{cfg['D']} bf16 "
+                f"K{cfg['topk']} + witness S{cfg['witness']['S']}")
+    if workload == "decode":
+        return (f"decode {cfg['n_q']} ragged rows (sum L {cfg['n_k']}) fp8 keys H{cfg['H']} "
+                f"D{cfg['D']} K{cfg['topk']} + witness S{cfg['witness']['S']}")
+    return workload
+
+
+def bench_block(args):
+    import numpy as np
+    import torch
+
+    import oracle
+    import sparse_attention_indexer_02_amd as si
+    import synth
+    cfg = synth.block()
+    dev = torch.device("cuda", 0)
+    q = torch.from_numpy(cfg["q"]).to(dev)
+    k = torch.from_numpy(cfg["k"]).to(dev)
+    pos = torch.from_numpy(cfg["query_pos"]).to(dev)
+    H, D, bs = cfg["H"], cfg["D"], cfg["block_size"]
+    width = cfg["out_width"]
+    out = torch.empty((cfg["n_q"], H, width), dtype=torch.int32, device=dev)
+    cnt = torch.empty((cfg["n_q"], H), dtype=torch.int32, device=dev)
+    ws = torch.empty(si.lib().block_sparse_select_workspace(cfg["n_q"], H, cfg["n_pos"], bs),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        si.block_sparse_select(q, k, pos, block_size=bs, top_blocks=cfg["top_blocks"],
+                               init_blocks=cfg["init_blocks"], local_blocks=cfg["local_blocks"],
+                               out_width=width, out_blocks=out, out_count=cnt, workspace=ws)
+
+    wall_ms, per = timed_steps([("select", step)], args.steps, args.warmup)
+    pos_np = np.minimum(cfg["query_pos"], cfg["n_pos"] - 1)
+    dots = int((pos_np + 1).sum()) * H  # (query, head, visible position) dots
+    ops = dots * 2.0 * D
+    ach = ops / per["select"] / 1e9
+    out_d = dict(metric="block-sparse (query, head, position) dots scored+selected /sec",
+                 value=dots / (wall_ms / 1e3), unit="dots/s", n_gpus=1, steps=args.steps,
+                 warmup=args.warmup, ms_per_step=wall_ms, higher_is_better=True,
+                 scaling="weak", vs_baseline=None, dtype="f32", data="synthetic",
+                 config=dict(workload=f"block-sparse select {cfg['n_q']} queries x "
+                                      f"{cfg['n_pos']} positions, {H} KV heads, D{D}, "
+                                      f"block {bs}, top {cfg['top_blocks']}"),
+                 roofline=dict(bound="alu", achieved=ach, peak=PEAK_VALU_TOPS, unit="TFLOP/s",
+                               frac=ach / PEAK_VALU_TOPS,
+                               traffic=counters_for("block_select.hip", "block"),
+                               kernel="block_max"))
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        n = 4
+        while True:
+            rows = np.linspace(0, cfg["n_q"] - 1, n).astype(np.int32)
+            t0 = time.perf_counter()
+            oracle.block_select_rows(cfg, rows)
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds * 0.5 or n >= cfg["n_q"]:
+                break
+            n = min(cfg["n_q"], int(n * min(8.0, max(2.0, args.cpu_seconds / max(el, 1e-3)))))
+        d = int((pos_np[rows] + 1).sum()) * H
+        out_d["cpu_baseline"] = dict(value=d / el, unit="dots/s", cores=oracle.num_threads(),
+                                     kind="oracle",
+                                     sample=f"{len(rows)} evenly spaced queries ({d} dots, "
+                                            f"{el:.1f} s)")
+    return out_d
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill",
+                    choices=["prefill", "decode", "dosa", "dosa_structured", "block"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps(dict(metric=METRIC, error="this build measures one GPU; multi-GPU "
+                              "row/key sharding is described in DESIGN.md and not run",
+                              n_gpus=args.gpus)))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import synth
+    if args.workload == "block":
+        out = bench_block(args)
+    elif args.workload in ("dosa", "dosa_structured"):
+        out = bench_dosa(args)
+    else:
+        log(f"generating {args.workload} inputs")
+        cfg = synth.prefill() if args.workload == "prefill" else synth.decode()
+        out = bench_indexer(args, cfg, args.workload)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -100,6 +100,25 @@ si_status idx_score_topk(const void* q, si_dtype q_dtype, const void* k, si_dtyp
                          size_t workspace_bytes, hipStream_t stream);
 size_t idx_score_topk_workspace(int32_t n_q, int32_t H, int32_t D, int64_t max_vis, int32_t topk);
 
+/* The two stages of idx_score_topk, for callers that keep the score rows
+ * (the notes' section 5 names score writeback and the selection input as
+ * costs of their own).
+ *
+ * idx_score: arguments as idx_score_topk; writes s[r, j] for j < vis_r into
+ *   out_scores[r * score_stride + j] (f32, device, score_stride >= max_vis);
+ *   entries j >= vis_r are not written.
+ * rows_topk: top-K of each row's first vis_r scores (vis_r clamped as in
+ *   idx_score_topk from vis_len / k_row_offset / n_k / max_vis), written as
+ *   idx_score_topk writes them.  scores rows at r * score_stride. */
+si_status idx_score(const void* q, si_dtype q_dtype, const void* k, si_dtype k_dtype,
+                    const float* k_scale, const float* w, int64_t w_row_stride,
+                    const int64_t* k_row_offset, const int32_t* vis_len, int32_t n_q, int32_t H,
+                    int32_t D, int64_t n_k, int64_t max_vis, float* out_scores,
+                    int64_t score_stride, hipStream_t stream);
+si_status rows_topk(const float* scores, int64_t score_stride, const int32_t* vis_len,
+                    const int64_t* k_row_offset, int64_t n_k, int64_t max_vis, int32_t n_rows,
+                    int32_t topk, int32_t* out_idx, float* out_score, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ *
  * dosa_prune_topk
  *

@@ -116,6 +116,11 @@ def problem(cfg):
     return _Keep(cfg)
 
 
+def visible(kp, r: int) -> int:
+    """Visible key count of row r (the clamped vis_len)."""
+    return lib().orc_visible(C.byref(kp.P), r)
+
+
 def e4m3fn_to_double(b: int) -> float:
     return lib().orc_e4m3fn_to_double(b)
 

@@ -44,6 +44,9 @@ SIGNATURES = {
     "idx_score_topk": (i32, [vp, i32, vp, i32, vp, vp, i64, vp, vp, i32, i32, i32, i64, i64, i32,
                              vp, vp, vp, sz, vp]),
     "idx_score_topk_workspace": (sz, [i32, i32, i32, i64, i32]),
+    "idx_score": (i32, [vp, i32, vp, i32, vp, vp, i64, vp, vp, i32, i32, i32, i64, i64, vp, i64,
+                        vp]),
+    "rows_topk": (i32, [vp, i64, vp, vp, i64, i64, i32, i32, vp, vp, vp]),
     "dosa_prune_topk": (i32, [vp, vp, i32, vp, i64, vp, i32, i32, i32, i64, i32, vp, vp, vp, vp,
                               vp, sz, vp]),
     "dosa_prune_topk_workspace": (sz, [i32, i32, i32, i64, i32, vp]),
@@ -148,6 +151,50 @@ def idx_score_topk(q, k, w, vis_len, topk, *, k_scale=None, k_row_offset=None, m
                               _ptr(vis_len), n_q, H, D, n_k, max_vis, topk, _ptr(out_idx),
                               _ptr(out_score), _ptr(ws), ws_bytes, _stream(dev))
     _check(st, "idx_score_topk")
+    return out_idx, out_score
+
+
+def idx_score(q, k, w, vis_len, *, k_scale=None, k_row_offset=None, max_vis=None,
+              out_scores=None):
+    """Score rows only: out_scores [n_q, max_vis] f32 (entries past vis_r untouched)."""
+    _dev_tensor(q, "q")
+    _dev_tensor(k, "k")
+    _dev_tensor(w, "w", torch.float32)
+    _dev_tensor(vis_len, "vis_len", torch.int32)
+    dev = q.device
+    n_q, H, D = q.shape
+    n_k = k.shape[0]
+    if max_vis is None:
+        max_vis = n_k if k_row_offset is None else (int(vis_len.max().item()) if n_q else 0)
+    if out_scores is None:
+        out_scores = torch.empty((n_q, max_vis), dtype=torch.float32, device=dev)
+    stride = out_scores.shape[1] if out_scores.dim() == 2 else max_vis
+    st = lib().idx_score(_ptr(q), _dtype_code(q, "q"), _ptr(k), _dtype_code(k, "k"),
+                         _ptr(k_scale), _ptr(w), H if w.dim() == 2 else 0, _ptr(k_row_offset),
+                         _ptr(vis_len), n_q, H, D, n_k, max_vis, _ptr(out_scores), stride,
+                         _stream(dev))
+    _check(st, "idx_score")
+    return out_scores
+
+
+def rows_topk(scores, vis_len, topk, *, k_row_offset=None, n_k=None, max_vis=None,
+              out_idx=None, out_score=None, want_scores=True):
+    """Top-K of each score row's first vis_r entries; returns (idx, scores|None)."""
+    _dev_tensor(scores, "scores", torch.float32)
+    _dev_tensor(vis_len, "vis_len", torch.int32)
+    dev = scores.device
+    n_rows, stride = scores.shape
+    if max_vis is None:
+        max_vis = stride
+    if n_k is None:
+        n_k = max_vis
+    if out_idx is None:
+        out_idx = torch.empty((n_rows, topk), dtype=torch.int32, device=dev)
+    if out_score is None and want_scores:
+        out_score = torch.empty((n_rows, topk), dtype=torch.float32, device=dev)
+    st = lib().rows_topk(_ptr(scores), stride, _ptr(vis_len), _ptr(k_row_offset), n_k, max_vis,
+                         n_rows, topk, _ptr(out_idx), _ptr(out_score), _stream(dev))
+    _check(st, "rows_topk")
     return out_idx, out_score
 
 

@@ -50,31 +50,77 @@ size_t idx_score_topk_workspace(int32_t n_q, int32_t H, int32_t D, int64_t max_v
   return score_ws_bytes(n_q, max_vis);
 }
 
+// Checks shared by idx_score and idx_score_topk; fills `sa` (scores unset).
+static si_status check_score_args(const void* q, si_dtype q_dtype, const void* k,
+                                  si_dtype k_dtype, const float* k_scale, const float* w,
+                                  int64_t w_row_stride, const int64_t* k_row_offset,
+                                  const int32_t* vis_len, int32_t n_q, int32_t H, int32_t D,
+                                  int64_t n_k, int64_t max_vis, ScoreArgs* sa) {
+  if (n_q < 0 || H < 1 || D < 1 || n_k < 0 || max_vis < 0 || w_row_stride < 0)
+    return SI_ERR_INVALID_ARGUMENT;
+  if (q_dtype != SI_F32 && q_dtype != SI_BF16) return SI_ERR_UNSUPPORTED_DTYPE;
+  if (k_dtype != SI_F32 && k_dtype != SI_BF16 && k_dtype != SI_FP8_E4M3FN)
+    return SI_ERR_UNSUPPORTED_DTYPE;
+  if (max_vis > INT32_MAX) return SI_ERR_INVALID_ARGUMENT;  // row-relative ids are int32
+  sa->q = q; sa->q_dtype = q_dtype; sa->k = k; sa->k_dtype = k_dtype; sa->k_scale = k_scale;
+  sa->w = w; sa->w_row_stride = w_row_stride; sa->k_row_offset = k_row_offset;
+  sa->vis_len = vis_len; sa->n_q = n_q; sa->H = H; sa->D = D; sa->n_k = n_k;
+  sa->max_vis = max_vis; sa->scores = nullptr; sa->score_stride = max_vis;
+  if (!score_mfma_supported(*sa) && !generic_shape_ok(H, D)) return SI_ERR_INVALID_ARGUMENT;
+  if (n_q == 0) return SI_OK;
+  if (!q || !k || !w || !vis_len) return SI_ERR_INVALID_ARGUMENT;
+  if (k_dtype == SI_FP8_E4M3FN && !k_scale) return SI_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned4(w)) return SI_ERR_INVALID_ARGUMENT;
+  return SI_OK;
+}
+
+si_status idx_score(const void* q, si_dtype q_dtype, const void* k, si_dtype k_dtype,
+                    const float* k_scale, const float* w, int64_t w_row_stride,
+                    const int64_t* k_row_offset, const int32_t* vis_len, int32_t n_q, int32_t H,
+                    int32_t D, int64_t n_k, int64_t max_vis, float* out_scores,
+                    int64_t score_stride, hipStream_t stream) {
+  ScoreArgs sa;
+  si_status s = check_score_args(q, q_dtype, k, k_dtype, k_scale, w, w_row_stride, k_row_offset,
+                                 vis_len, n_q, H, D, n_k, max_vis, &sa);
+  if (s != SI_OK || n_q == 0) return s;
+  if (!out_scores || !aligned4(out_scores) || score_stride < max_vis)
+    return SI_ERR_INVALID_ARGUMENT;
+  sa.scores = out_scores;
+  sa.score_stride = score_stride;
+  return launch_score(sa, stream) == hipSuccess ? SI_OK : SI_ERR_DEVICE;
+}
+
+si_status rows_topk(const float* scores, int64_t score_stride, const int32_t* vis_len,
+                    const int64_t* k_row_offset, int64_t n_k, int64_t max_vis, int32_t n_rows,
+                    int32_t topk, int32_t* out_idx, float* out_score, hipStream_t stream) {
+  if (n_rows < 0 || n_k < 0 || max_vis < 0 || max_vis > INT32_MAX || topk < 1 ||
+      topk > kMaxTopk || score_stride < max_vis)
+    return SI_ERR_INVALID_ARGUMENT;
+  if (n_rows == 0) return SI_OK;
+  if ((max_vis > 0 && !scores) || !vis_len || !out_idx || !aligned4(out_idx) ||
+      (out_score && !aligned4(out_score)) || (scores && !aligned4(scores)))
+    return SI_ERR_INVALID_ARGUMENT;
+  TopkArgs ta;
+  ta.scores = scores; ta.stride = score_stride; ta.vis_len = vis_len;
+  ta.k_row_offset = k_row_offset; ta.n_k = n_k; ta.max_vis = max_vis; ta.n_rows = n_rows;
+  ta.K = topk; ta.out_idx = out_idx; ta.out_score = out_score; ta.id_map = nullptr;
+  return launch_topk(ta, stream) == hipSuccess ? SI_OK : SI_ERR_DEVICE;
+}
+
 si_status idx_score_topk(const void* q, si_dtype q_dtype, const void* k, si_dtype k_dtype,
                          const float* k_scale, const float* w, int64_t w_row_stride,
                          const int64_t* k_row_offset, const int32_t* vis_len, int32_t n_q,
                          int32_t H, int32_t D, int64_t n_k, int64_t max_vis, int32_t topk,
                          int32_t* out_idx, float* out_score, void* workspace,
                          size_t workspace_bytes, hipStream_t stream) {
-  if (n_q < 0 || H < 1 || D < 1 || n_k < 0 || max_vis < 0 || topk < 1 || topk > kMaxTopk ||
-      w_row_stride < 0)
-    return SI_ERR_INVALID_ARGUMENT;
-  if (q_dtype != SI_F32 && q_dtype != SI_BF16) return SI_ERR_UNSUPPORTED_DTYPE;
-  if (k_dtype != SI_F32 && k_dtype != SI_BF16 && k_dtype != SI_FP8_E4M3FN)
-    return SI_ERR_UNSUPPORTED_DTYPE;
-  if (max_vis > INT32_MAX) return SI_ERR_INVALID_ARGUMENT;  // row-relative ids are int32
-  if (n_q == 0) return SI_OK;
-  if (!q || !k || !w || !vis_len || !out_idx) return SI_ERR_INVALID_ARGUMENT;
-  if (k_dtype == SI_FP8_E4M3FN && !k_scale) return SI_ERR_INVALID_ARGUMENT;
-  if (!aligned16(q) || !aligned16(k) || !aligned4(w) || !aligned4(out_idx) ||
-      (out_score && !aligned4(out_score)))
-    return SI_ERR_INVALID_ARGUMENT;
   ScoreArgs sa;
-  sa.q = q; sa.q_dtype = q_dtype; sa.k = k; sa.k_dtype = k_dtype; sa.k_scale = k_scale;
-  sa.w = w; sa.w_row_stride = w_row_stride; sa.k_row_offset = k_row_offset; sa.vis_len = vis_len;
-  sa.n_q = n_q; sa.H = H; sa.D = D; sa.n_k = n_k; sa.max_vis = max_vis;
-  sa.scores = nullptr; sa.score_stride = max_vis;
-  if (!score_mfma_supported(sa) && !generic_shape_ok(H, D)) return SI_ERR_INVALID_ARGUMENT;
+  si_status s = check_score_args(q, q_dtype, k, k_dtype, k_scale, w, w_row_stride, k_row_offset,
+                                 vis_len, n_q, H, D, n_k, max_vis, &sa);
+  if (s != SI_OK) return s;
+  if (topk < 1 || topk > kMaxTopk) return SI_ERR_INVALID_ARGUMENT;
+  if (n_q == 0) return SI_OK;
+  if (!out_idx || !aligned4(out_idx) || (out_score && !aligned4(out_score)))
+    return SI_ERR_INVALID_ARGUMENT;
   const size_t need = score_ws_bytes(n_q, max_vis);
   if (need && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return SI_ERR_WORKSPACE_TOO_SMALL;
