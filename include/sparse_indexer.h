@@ -135,14 +135,16 @@ si_status rows_topk(const float* scores, int64_t score_stride, const int32_t* vi
  * error states trigger an exact recovery.
  *
  * Prefill layout: keys are shared by all rows (no row offsets), q and k are
- * SI_BF16, w as in idx_score_topk, row r sees keys [0, vis_r).
+ * SI_BF16, D is 64 or 128, 1 <= H <= 64, w as in idx_score_topk, row r sees
+ * keys [0, vis_r) with vis_r = clamp(vis_len[r], 0, n_k).
  * The result is bit-identical to idx_score_topk on the same device for the
  * same inputs (idx and scores).
  *
- *  params->n_seeds           seeds (>= topk); 12288 on the page.
- *  params->n_rep_queries     representative rows for the cold prior (>= 1).
- *  params->rep_topk          top list length per representative row.
- *  params->kept_heads        heads scored exactly in the bound (<= 16, < H).
+ *  params->n_seeds           seeds, topk <= n_seeds <= n_k; 12288 on the page.
+ *  params->n_rep_queries     representative rows for the cold prior (1..64),
+ *                            row round(i (n_q-1)/(R-1)) for i = 0..R-1.
+ *  params->rep_topk          top list length per representative row (1..4096).
+ *  params->kept_heads        heads scored exactly in the bound (0..min(31, H)).
  *  params->neg_active_frac   omitted negative heads whose activation
  *                            frequency over the seeds is >= this are
  *                            aggregated; the rest are dropped (safe).
@@ -150,8 +152,11 @@ si_status rows_topk(const float* scores, int64_t score_stride, const int32_t* vi
  *                            visible to every row, or NULL for the cold
  *                            prior (the hook a prior from earlier queries
  *                            would use).
- *  params->survivor_capacity survivors a row may keep (>= 1); a row with
+ *  params->survivor_capacity survivors a row may keep (1..8192); a row with
  *                            more takes the exact unpruned path.
+ * The workspace (dosa_prune_topk_workspace) holds the seed scores
+ * [n_q, n_seeds], survivor lists [n_q, capacity] and, for the exact path,
+ * full score rows [n_q, n_k] (f32).
  *  stats (optional, device pointers, each may be NULL): tau [n_q],
  *        n_survivors [n_q] (keys passing the bound), fallback [n_q] (1 when
  *        the row took the exact path).

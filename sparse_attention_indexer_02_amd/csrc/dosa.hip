@@ -1,0 +1,910 @@
+// DoSA certified prune (DoSA reading notes, sections 2-4), prefill layout.
+//
+// Pipeline, all on the caller's stream, every grid sized from host-known
+// bounds (no device-to-host reads):
+//   init        common visible prefix c, flags, zeroed counters
+//   cold prior  representative rows t_i = round(i (n_q-1)/(R-1)) scored over
+//               [0, c) and top-rep_topk'd; key occurrence counts; seeds =
+//               n_seeds keys of [0, c) by (count desc, key asc), kept in
+//               ascending key order (section 4).  A caller prior replaces it.
+//   seed pass   every row x every seed with the shared score micro-kernel,
+//               plus per-head activation counts and ReLU sums; seed top-K by
+//               (score desc, key asc); tau = its K-th score (section 2.1).
+//   plan        per row: kept heads = the kept_heads largest
+//               |w_h| * mean_seeds max(x_h, 0); each omitted positive head
+//               anchors on the kept head of smallest residual under the
+//               clamped projection beta = max(0, q_h.q_j/|q_j|^2) (section
+//               3.1); folded weights w'_j = w_j + sum beta_h w_h; residual
+//               R = sum w_h |d_h|; omitted negative heads active on at least
+//               neg_active_frac of the seeds aggregate into a_A = sum |w_h| q_h
+//               (section 3.2), carried in bf16 as a_hat.  All in fp64.
+//   bound       MFMA over the 32-row plan tile (kept heads, a_hat, zeros):
+//               U = sum w'_j max(x_j,0) - max(a_hat.k, 0) + C_r |k|; a key
+//               survives iff U >= tau (section 2.2).  C_r = R + |a_A - a_hat|
+//               + 2^-10 (sum_h |w_h||q_h| + sum_J |w'_j||q_j| + |a_hat| + R +
+//               |a_A - a_hat|): ReLU is 1-Lipschitz, so the a_hat term costs
+//               |a_A - a_hat||k|, and 2^-10 |.||k| dominates every fp32
+//               rounding of the computed score and of U (fp32 MFMA sums of
+//               128 exact products err by at most ~2^-16 |q||k|).  So U is
+//               at least the score this device computes.
+//   compact     ballot bitmap -> ascending survivor ids; more than
+//               survivor_capacity sends the row to the exact path.
+//   rescore     survivors with the shared micro-kernel; keep s >= tau.
+//   merge       seed top-K (sorted) merged with the sorted kept survivors;
+//               first K by (score desc, key asc).
+//   fallback    listed rows (overflow, or every row when c < n_seeds or a
+//               caller prior is invalid) take the unpruned score + top-K.
+// The result equals idx_score_topk's bit for bit: scores come from one
+// micro-kernel, and every key of the unpruned top-K is a seed in the seed
+// top-K or a survivor with s >= tau (its U >= s >= K-th overall >= tau).
+#include <math.h>
+
+#include "score_micro.hpp"
+
+namespace si {
+
+struct DosaCtx {
+  int32_t c;                // common visible prefix
+  int32_t global_fallback;  // every row takes the exact path
+  int32_t n_fallback;       // length of the fallback row list
+  int32_t pad[61];
+};
+
+struct DosaLayout {
+  size_t ctx, rep_q, rep_w, rep_vis, rep_scores, rep_ids, counts, seeds, seed_mask, seed_keys,
+      seed_scores, stat_cnt, stat_sum, top_idx, top_score, plan_a, plan_w, plan_c, knorm, bitmap,
+      surv_ids, surv_cnt, row_fb, kept_score, kept_id, kept_cnt, fb_list, fb_scores, total;
+};
+
+static size_t au(size_t x) { return (x + 255) / 256 * 256; }
+
+static DosaLayout dosa_layout(int32_t n_q, int32_t H, int32_t D, int64_t n_k, int32_t topk,
+                              const si_dosa_params* p) {
+  DosaLayout L;
+  size_t o = 0;
+  const size_t nq = (size_t)n_q, nk = (size_t)n_k, R = (size_t)p->n_rep_queries;
+  const size_t ns = (size_t)p->n_seeds, cap = (size_t)p->survivor_capacity;
+  const size_t words = (nk + 31) / 32;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += au(bytes);
+    return at;
+  };
+  L.ctx = take(sizeof(DosaCtx));
+  L.rep_q = take(R * H * D * 2);
+  L.rep_w = take(R * H * 4);
+  L.rep_vis = take(R * 4);
+  L.rep_scores = take(R * nk * 4);
+  L.rep_ids = take(R * (size_t)p->rep_topk * 4);
+  L.counts = take(nk * 4);
+  L.seeds = take(ns * 4);
+  L.seed_mask = take(words * 4);
+  L.seed_keys = take(ns * D * 2);
+  L.seed_scores = take(nq * ns * 4);
+  L.stat_cnt = take(nq * H * 4);
+  L.stat_sum = take(nq * H * 4);
+  L.top_idx = take(nq * topk * 4);
+  L.top_score = take(nq * topk * 4);
+  L.plan_a = take(nq * 32 * D * 2);
+  L.plan_w = take(nq * 32 * 4);
+  L.plan_c = take(nq * 4);
+  L.knorm = take(nk * 4);
+  L.bitmap = take(nq * words * 4);
+  L.surv_ids = take(nq * cap * 4);
+  L.surv_cnt = take(nq * 4);
+  L.row_fb = take(nq * 4);
+  L.kept_score = take(nq * cap * 4);
+  L.kept_id = take(nq * cap * 4);
+  L.kept_cnt = take(nq * 4);
+  L.fb_list = take(nq * 4);
+  L.fb_scores = take(nq * nk * 4);
+  L.total = o;
+  return L;
+}
+
+constexpr int kMaxRep = 64;
+constexpr int kMaxCapacity = 8192;
+
+// ---------------------------------------------------------------------------
+__global__ void fill_i32(int32_t* p, int64_t n, int32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+__global__ __launch_bounds__(1024) void dosa_init(DosaCtx* ctx, const int32_t* vis_len, int n_q,
+                                                  int64_t n_k, int n_seeds, int32_t* rep_vis,
+                                                  int R) {
+  __shared__ int red[32];
+  int m = INT32_MAX;
+  for (int r = threadIdx.x; r < n_q; r += 1024) {
+    int64_t off;
+    int v = (int)visible_len(vis_len, nullptr, r, n_k, n_k, &off);
+    m = v < m ? v : m;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    int y = __shfl_xor(m, o, 64);
+    m = y < m ? y : m;
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int c = INT32_MAX;
+    for (int i = 0; i < 1024 / 64; ++i) c = red[i] < c ? red[i] : c;
+    if (n_q == 0) c = 0;
+    ctx->c = c;
+    ctx->global_fallback = (c < n_seeds) ? 1 : 0;
+    ctx->n_fallback = 0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < R; i += 1024) rep_vis[i] = ctx->c;
+}
+
+// Representative rows t_i = round(i (n_q - 1) / (R - 1)), gathered densely.
+__global__ __launch_bounds__(256) void dosa_gather_rep(const uint16_t* q, const float* w,
+                                                       int64_t w_stride, int n_q, int H, int D,
+                                                       int R, uint16_t* rep_q, float* rep_w) {
+  const int i = blockIdx.x;
+  int t = 0;
+  if (R > 1 && n_q > 1)
+    t = (int)((2LL * i * (n_q - 1) + (R - 1)) / (2LL * (R - 1)));
+  for (int e = threadIdx.x; e < H * D; e += 256) rep_q[(int64_t)i * H * D + e] =
+      q[(int64_t)t * H * D + e];
+  for (int h = threadIdx.x; h < H; h += 256) rep_w[(int64_t)i * H + h] = w[(int64_t)t * w_stride + h];
+}
+
+__global__ void dosa_count(const int32_t* rep_ids, int64_t n, int32_t* counts, int64_t n_k) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int id = rep_ids[i];
+    if (id >= 0 && id < n_k) atomicAdd(&counts[id], 1);
+  }
+}
+
+// Seeds: the caller's (validated) or the first n_seeds keys of [0, c) by
+// (count desc, key asc), written ascending; the seed bitmap is set.
+__global__ __launch_bounds__(1024) void dosa_select_seeds(DosaCtx* ctx, const int32_t* counts,
+                                                          int R, int n_seeds,
+                                                          const int32_t* caller_seeds,
+                                                          int32_t* seeds, uint32_t* seed_mask) {
+  constexpr int T = 1024;
+  __shared__ int ge[kMaxRep + 2];
+  __shared__ int red[T / 64 + 4];
+  __shared__ int bad;
+  if (ctx->global_fallback) return;
+  const int c = ctx->c;
+  if (caller_seeds) {
+    if (threadIdx.x == 0) bad = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n_seeds; i += T) {
+      int id = caller_seeds[i];
+      bool ok = id >= 0 && id < c && (i == 0 || caller_seeds[i - 1] < id);
+      if (!ok) bad = 1;
+      seeds[i] = ok ? id : 0;
+      if (ok) atomicOr(&seed_mask[id >> 5], 1u << (id & 31));
+    }
+    __syncthreads();
+    if (threadIdx.x == 0 && bad) ctx->global_fallback = 1;
+    return;
+  }
+  for (int v = threadIdx.x; v <= R + 1; v += T) ge[v] = 0;
+  __syncthreads();
+  for (int j = threadIdx.x; j < c; j += T) {
+    int cnt = counts[j];
+    cnt = cnt > R ? R : cnt;
+    atomicAdd(&ge[cnt], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {  // ge[v] := #{count >= v}
+    for (int v = R - 1; v >= 0; --v) ge[v] += ge[v + 1];
+  }
+  __syncthreads();
+  int vstar = 0;
+  for (int v = R; v >= 0; --v)
+    if (ge[v] >= n_seeds) {
+      vstar = v;
+      break;
+    }
+  const int need_eq = n_seeds - ge[vstar + 1];  // taken among count == vstar, by key
+  int eq_before = 0, pos_before = 0;
+  for (int base = 0; base < c; base += T) {
+    int j = base + threadIdx.x;
+    int cnt = j < c ? (counts[j] > R ? R : counts[j]) : -1;
+    int is_eq = (cnt == vstar) ? 1 : 0;
+    int tot_eq;
+    int eq_rank = eq_before + block_excl_scan<T>(is_eq, red, &tot_eq);
+    int sel = (j < c) && (cnt > vstar || (is_eq && eq_rank < need_eq)) ? 1 : 0;
+    int tot_sel;
+    int pos = pos_before + block_excl_scan<T>(sel, red, &tot_sel);
+    if (sel) {
+      seeds[pos] = j;
+      atomicOr(&seed_mask[j >> 5], 1u << (j & 31));
+    }
+    eq_before += tot_eq;
+    pos_before += tot_sel;
+  }
+}
+
+__global__ __launch_bounds__(256) void dosa_gather_seed_keys(const DosaCtx* ctx,
+                                                             const uint16_t* k,
+                                                             const int32_t* seeds, int n_seeds,
+                                                             int D, uint16_t* seed_keys) {
+  if (ctx->global_fallback) return;
+  const int cpk = D / 8;  // 16-byte chunks per key
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < (int64_t)n_seeds * cpk;
+       e += (int64_t)gridDim.x * 256) {
+    int i = (int)(e / cpk), c = (int)(e % cpk);
+    reinterpret_cast<u32x4*>(seed_keys + (int64_t)i * D)[c] =
+        reinterpret_cast<const u32x4*>(k + (int64_t)seeds[i] * D)[c];
+  }
+}
+
+// Seed scoring: every row against every seed key (dense [n_seeds, D] tile
+// source), the shared micro-kernel, plus per-head activation statistics.
+template <int MT, int KS, int QPW>
+__global__ __launch_bounds__(256, 2) void dosa_seed_score(
+    const DosaCtx* ctx, const uint16_t* __restrict__ q, const uint16_t* __restrict__ sk,
+    const float* __restrict__ w, int64_t w_stride, int n_q, int H, int n_seeds,
+    float* __restrict__ seed_scores, int32_t* __restrict__ stat_cnt, float* __restrict__ stat_sum) {
+  constexpr int D = 16 * KS;
+  constexpr int ROWB = D * 2 + 16;
+  constexpr int CPK = D * 2 / 16;
+  constexpr int CHUNKS = 32 * CPK;
+  constexpr int CPT = (CHUNKS + 255) / 256;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][32 * ROWB];
+  if (ctx->global_fallback) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r0 = (int)blockIdx.x * 4 * QPW + wave * QPW;
+
+  bf16x8 a[QPW][MT][KS];
+  float wv[QPW][MT][16];
+  int cnt[QPW][MT][16];
+  float rs[QPW][MT][16];
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    load_q_frag<MT, KS>(q, r0 + i, H, r0 + i < n_q, a[i]);
+    load_w_frag<MT>(w, w_stride, r0 + i, H, r0 + i < n_q, wv[i]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        cnt[i][mt][v] = 0;
+        rs[i][mt][v] = 0.0f;
+      }
+  }
+  const int ntiles = (n_seeds + 31) / 32;
+  u32x4 pre[CPT];
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      int ch = threadIdx.x + 256 * c;
+      int key = ch / CPK, part = ch % CPK;
+      int j = t * 32 + key;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ch < CHUNKS && j < n_seeds) v = reinterpret_cast<const u32x4*>(sk + (int64_t)j * D)[part];
+      pre[c] = v;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      int ch = threadIdx.x + 256 * c;
+      int key = ch / CPK, part = ch % CPK;
+      if (ch < CHUNKS) *reinterpret_cast<u32x4*>(&lds[buf][key * ROWB + part * 16]) = pre[c];
+    }
+  };
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) fetch(t + 1);
+    const unsigned char* brow = &lds[buf][(lane & 31) * ROWB + (lane >> 5) * 16];
+    f32x16 acc[QPW][MT];
+    mfma_tiles<QPW, MT, KS>(
+        a, [&](int s) { return as_bf16x8(*reinterpret_cast<const u32x4*>(brow + 32 * s)); },
+        acc);
+    const int j = t * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      float s = head_reduce<MT>(acc[i], wv[i]);
+      // padding keys are zero: x = 0 adds nothing to either statistic
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float x = acc[i][mt][v];
+          cnt[i][mt][v] += x > 0.0f ? 1 : 0;
+          rs[i][mt][v] += __builtin_fmaxf(x, 0.0f);
+        }
+      if (lane < 32 && r0 + i < n_q && j < n_seeds)
+        seed_scores[(int64_t)(r0 + i) * n_seeds + j] = s;
+    }
+    if (t + 1 < ntiles) stash(buf ^ 1);
+    __syncthreads();
+  }
+  // reduce the statistics over the 32 key lanes of each half-wave
+#pragma unroll
+  for (int i = 0; i < QPW; ++i)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        int c = cnt[i][mt][v];
+        float f = rs[i][mt][v];
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+          c += __shfl_xor(c, o, 64);
+          f += __shfl_xor(f, o, 64);
+        }
+        int h = mt * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if ((lane & 31) == 0 && r0 + i < n_q && h < H) {
+          stat_cnt[(int64_t)(r0 + i) * H + h] = c;
+          stat_sum[(int64_t)(r0 + i) * H + h] = f;
+        }
+      }
+}
+
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  float f = (float)x;  // the f32 rounding is exact for the bf16 grid's decision below
+  uint32_t u = __float_as_uint(f);
+  // round the f32 to bf16 by nearest-even on the exact double: compare the
+  // two bf16 neighbours of x directly
+  uint32_t lo = u & 0xFFFF0000u;
+  float flo = __uint_as_float(lo);
+  float fhi = __uint_as_float(lo + 0x10000u);
+  double dlo = fabs(x - (double)flo), dhi = fabs(x - (double)fhi);
+  // for negative x, lo is the larger magnitude neighbour toward zero
+  uint32_t pick;
+  if (dlo < dhi) pick = lo;
+  else if (dhi < dlo) pick = lo + 0x10000u;
+  else pick = ((lo >> 16) & 1u) ? lo + 0x10000u : lo;
+  return (uint16_t)(pick >> 16);
+}
+
+// Per-row plan (fp64).  One workgroup per row.
+constexpr int kPlanThreads = 256;
+__global__ __launch_bounds__(kPlanThreads) void dosa_plan(
+    const DosaCtx* ctx, const uint16_t* __restrict__ q, const float* __restrict__ w,
+    int64_t w_stride, int H, int D, int n_seeds, int kept_heads, float neg_frac,
+    const int32_t* __restrict__ stat_cnt, const float* __restrict__ stat_sum,
+    uint16_t* __restrict__ plan_a, float* __restrict__ plan_w, float* __restrict__ plan_c) {
+  __shared__ double qd[64 * 128];
+  __shared__ double qq[64], wf[64], dn[64], beta[64], agg[128];
+  __shared__ float imp[64];
+  __shared__ int role[64], anchor[64], kept_list[32];
+  __shared__ int n_kept;
+  if (ctx->global_fallback) return;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  for (int e = tid; e < H * D; e += kPlanThreads)
+    qd[e] = (double)__uint_as_float((uint32_t)q[(int64_t)r * H * D + e] << 16);
+  for (int h = tid; h < H; h += kPlanThreads)
+    imp[h] = fabsf(w[(int64_t)r * w_stride + h]) * (stat_sum[(int64_t)r * H + h] / (float)n_seeds);
+  __syncthreads();
+  if (tid < H) {
+    int h = tid, rank = 0;
+    for (int g = 0; g < H; ++g)
+      rank += (imp[g] > imp[h] || (imp[g] == imp[h] && g < h)) ? 1 : 0;
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) s += qd[h * D + d] * qd[h * D + d];
+    qq[h] = s;
+    const float wh = w[(int64_t)r * w_stride + h];
+    const float act = (float)stat_cnt[(int64_t)r * H + h] / (float)n_seeds;
+    role[h] = rank < kept_heads ? 1 : (wh > 0.0f ? 2 : (wh < 0.0f ? (act >= neg_frac ? 3 : 4) : 0));
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int n = 0;
+    for (int h = 0; h < H; ++h)
+      if (role[h] == 1) kept_list[n++] = h;
+    n_kept = n;
+  }
+  __syncthreads();
+  const int nk = n_kept;
+  // anchors of omitted positive heads: smallest residual, lower head on ties
+  if (tid < H) {
+    int h = tid;
+    anchor[h] = -1;
+    beta[h] = 0.0;
+    dn[h] = 0.0;
+    if (role[h] == 2) {
+      double best = INFINITY, bb = 0.0;
+      int bj = -1;
+      for (int t = 0; t < nk; ++t) {
+        int j = kept_list[t];
+        double g = 0.0;
+        for (int d = 0; d < D; ++d) g += qd[h * D + d] * qd[j * D + d];
+        double b = qq[j] > 0.0 ? g / qq[j] : 0.0;
+        b = b < 0.0 ? 0.0 : b;
+        double r2 = qq[h] - 2.0 * b * g + b * b * qq[j];
+        if (r2 < best) {
+          best = r2;
+          bb = b;
+          bj = j;
+        }
+      }
+      double s = 0.0;  // explicit |q_h - beta q_a|: no cancellation in the bound
+      for (int d = 0; d < D; ++d) {
+        double e = qd[h * D + d] - (bj >= 0 ? bb * qd[bj * D + d] : 0.0);
+        s += e * e;
+      }
+      anchor[h] = bj;
+      beta[h] = bb;
+      dn[h] = sqrt(s);
+    }
+  }
+  __syncthreads();
+  if (tid < H) {
+    int j = tid;
+    double f = 0.0;
+    if (role[j] == 1) {
+      f = (double)w[(int64_t)r * w_stride + j];
+      for (int h = 0; h < H; ++h)
+        if (role[h] == 2 && anchor[h] == j) f += (double)w[(int64_t)r * w_stride + h] * beta[h];
+    }
+    wf[j] = f;
+  }
+  for (int d = tid; d < D; d += kPlanThreads) {
+    double s = 0.0;
+    for (int h = 0; h < H; ++h)
+      if (role[h] == 3) s += fabs((double)w[(int64_t)r * w_stride + h]) * qd[h * D + d];
+    agg[d] = s;
+  }
+  __syncthreads();
+  uint16_t* pa = plan_a + (int64_t)r * 32 * D;
+  for (int e = tid; e < 32 * D; e += kPlanThreads) {
+    int row = e / D, d = e % D;
+    uint16_t v = 0;
+    if (row < nk) v = q[((int64_t)r * H + kept_list[row]) * D + d];
+    else if (row == nk) v = f64_to_bf16_rne(agg[d]);
+    pa[e] = v;
+  }
+  if (tid < 32) {
+    float v = 0.0f;
+    if (tid < nk) v = (float)wf[kept_list[tid]];
+    else if (tid == nk) v = -1.0f;
+    plan_w[(int64_t)r * 32 + tid] = v;
+  }
+  if (tid == 0) {
+    double R = 0.0, nw = 0.0, nwf = 0.0, err2 = 0.0, ah2 = 0.0;
+    for (int h = 0; h < H; ++h) {
+      double wh = (double)w[(int64_t)r * w_stride + h];
+      nw += fabs(wh) * sqrt(qq[h]);
+      if (role[h] == 2) R += wh * dn[h];
+      if (role[h] == 1) nwf += fabs(wf[h]) * sqrt(qq[h]);
+    }
+    for (int d = 0; d < D; ++d) {
+      double ah = (double)__uint_as_float((uint32_t)f64_to_bf16_rne(agg[d]) << 16);
+      err2 += (agg[d] - ah) * (agg[d] - ah);
+      ah2 += ah * ah;
+    }
+    double err = sqrt(err2), ahn = sqrt(ah2);
+    double C = R + err + 0x1p-10 * (nw + nwf + ahn + R + err);
+    plan_c[r] = __double2float_ru(C);
+  }
+}
+
+__global__ void dosa_knorm(const uint16_t* k, int64_t n_k, int D, float* knorm) {
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n_k;
+       j += (int64_t)gridDim.x * blockDim.x) {
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) {
+      double x = (double)__uint_as_float((uint32_t)k[j * D + d] << 16);
+      s += x * x;
+    }
+    knorm[j] = __double2float_ru(sqrt(s) * (1.0 + 0x1p-40));
+  }
+}
+
+// Bound scan: MFMA over the 32-row plan tile of QPW rows per wave, shared
+// key tiles through LDS; writes one 32-bit survivor mask per (row, tile).
+template <int KS, int QPW>
+__global__ __launch_bounds__(256, 2) void dosa_bound(
+    const DosaCtx* ctx, const uint16_t* __restrict__ plan_a, const float* __restrict__ plan_w,
+    const float* __restrict__ plan_c, const float* __restrict__ top_score, int topk,
+    const uint16_t* __restrict__ k, const float* __restrict__ knorm,
+    const uint32_t* __restrict__ seed_mask, const int32_t* __restrict__ vis_len, int n_q,
+    int64_t n_k, uint32_t* __restrict__ bitmap, int64_t words) {
+  constexpr int D = 16 * KS;
+  constexpr int QB = 4 * QPW;
+  constexpr int ROWB = D * 2 + 16;
+  constexpr int CPK = D * 2 / 16;
+  constexpr int CHUNKS = 32 * CPK;
+  constexpr int CPT = (CHUNKS + 255) / 256;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][32 * ROWB];
+  if (ctx->global_fallback) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = (n_q + QB - 1) / QB - 1 - (int)blockIdx.x;
+  const int r0 = g * QB;
+  int64_t vis[QPW];
+  float tau[QPW], cr[QPW];
+  int64_t end = 0;
+  for (int i = 0; i < QB; ++i) {
+    int r = r0 + i;
+    int64_t off, v = 0;
+    if (r < n_q) v = visible_len(vis_len, nullptr, r, n_k, n_k, &off);
+    end = v > end ? v : end;
+    if (i / QPW == wave) {
+      vis[i % QPW] = v;
+      tau[i % QPW] = r < n_q ? top_score[(int64_t)r * topk + topk - 1] : 0.0f;
+      cr[i % QPW] = r < n_q ? plan_c[r] : 0.0f;
+    }
+  }
+  if (end == 0) return;
+  bf16x8 a[QPW][1][KS];
+  float wv[QPW][1][16];
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    int r = r0 + wave * QPW + i;
+    load_q_frag<1, KS>(plan_a, r, 32, r < n_q, a[i]);
+    load_w_frag<1>(plan_w, 32, r, 32, r < n_q, wv[i]);
+  }
+  const int ntiles = (int)((end + 31) / 32);
+  u32x4 pre[CPT];
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      int ch = threadIdx.x + 256 * c;
+      int key = ch / CPK, part = ch % CPK;
+      int64_t j = (int64_t)t * 32 + key;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ch < CHUNKS && j < n_k) v = reinterpret_cast<const u32x4*>(k + j * D)[part];
+      pre[c] = v;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      int ch = threadIdx.x + 256 * c;
+      int key = ch / CPK, part = ch % CPK;
+      if (ch < CHUNKS) *reinterpret_cast<u32x4*>(&lds[buf][key * ROWB + part * 16]) = pre[c];
+    }
+  };
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) fetch(t + 1);
+    const unsigned char* brow = &lds[buf][(lane & 31) * ROWB + (lane >> 5) * 16];
+    f32x16 acc[QPW][1];
+    mfma_tiles<QPW, 1, KS>(
+        a, [&](int s) { return as_bf16x8(*reinterpret_cast<const u32x4*>(brow + 32 * s)); },
+        acc);
+    const int64_t j = (int64_t)t * 32 + (lane & 31);
+    const float kn = j < n_k ? knorm[j] : 0.0f;
+    const bool seed = j < n_k && ((seed_mask[j >> 5] >> (j & 31)) & 1u);
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      float u = head_reduce<1>(acc[i], wv[i]) + cr[i] * kn;
+      bool pass = lane < 32 && j < vis[i] && !seed && u >= tau[i];
+      uint64_t m = __ballot(pass);
+      int r = r0 + wave * QPW + i;
+      if (lane == 0 && r < n_q && (int64_t)t * 32 < vis[i])
+        bitmap[(int64_t)r * words + t] = (uint32_t)m;
+    }
+    if (t + 1 < ntiles) stash(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+// Bitmap -> ascending survivor ids (one workgroup per row).
+constexpr int kCompThreads = 256;
+__global__ __launch_bounds__(kCompThreads) void dosa_compact(
+    const DosaCtx* ctx, const uint32_t* __restrict__ bitmap, int64_t words,
+    const int32_t* __restrict__ vis_len, int64_t n_k, int cap, int32_t* __restrict__ surv_ids,
+    int32_t* __restrict__ surv_cnt, int32_t* __restrict__ row_fb) {
+  __shared__ int red[kCompThreads / 64 + 4];
+  const int r = blockIdx.x;
+  if (ctx->global_fallback) {
+    if (threadIdx.x == 0) {
+      surv_cnt[r] = 0;
+      row_fb[r] = 1;
+    }
+    return;
+  }
+  int64_t off;
+  const int64_t v = visible_len(vis_len, nullptr, r, n_k, n_k, &off);
+  const int64_t nw = (v + 31) / 32;
+  const int64_t per = (nw + kCompThreads - 1) / kCompThreads;
+  const int64_t w0 = (int64_t)threadIdx.x * per;
+  int mine = 0;
+  for (int64_t i = w0; i < w0 + per && i < nw; ++i) mine += __popc(bitmap[(int64_t)r * words + i]);
+  int total;
+  int pos = block_excl_scan<kCompThreads>(mine, red, &total);
+  const bool over = total > cap;
+  if (!over) {
+    for (int64_t i = w0; i < w0 + per && i < nw; ++i) {
+      uint32_t m = bitmap[(int64_t)r * words + i];
+      while (m) {
+        int b = __ffs(m) - 1;
+        m &= m - 1;
+        surv_ids[(int64_t)r * cap + pos++] = (int32_t)(i * 32 + b);
+      }
+    }
+  }
+  if (threadIdx.x == 0) {
+    surv_cnt[r] = total;
+    row_fb[r] = over ? 1 : 0;
+  }
+}
+
+// Exact rescoring of survivors with the shared micro-kernel (keys gathered
+// straight into the k-step layout).  One workgroup per row.
+template <int MT, int KS>
+__global__ __launch_bounds__(256) void dosa_rescore(
+    const DosaCtx* ctx, const uint16_t* __restrict__ q, const float* __restrict__ w,
+    int64_t w_stride, int H, const uint16_t* __restrict__ k, const float* __restrict__ top_score,
+    int topk, const int32_t* __restrict__ surv_ids, const int32_t* __restrict__ surv_cnt,
+    const int32_t* __restrict__ row_fb, int cap, float* __restrict__ kept_score,
+    int32_t* __restrict__ kept_id, int32_t* __restrict__ kept_cnt) {
+  constexpr int D = 16 * KS;
+  const int r = blockIdx.x;
+  if (ctx->global_fallback || row_fb[r]) return;
+  const int n = surv_cnt[r];
+  if (n == 0) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float tau = top_score[(int64_t)r * topk + topk - 1];
+  bf16x8 a[1][MT][KS];
+  float wv[MT][16];
+  load_q_frag<MT, KS>(q, r, H, true, a[0]);
+  load_w_frag<MT>(w, w_stride, r, H, true, wv);
+  for (int t0 = wave * 32; t0 < n; t0 += 4 * 32) {
+    const int i = t0 + (lane & 31);
+    const bool in = i < n;
+    const int id = in ? surv_ids[(int64_t)r * cap + i] : 0;
+    const u32x4* kb = reinterpret_cast<const u32x4*>(k + (int64_t)id * D);
+    f32x16 acc[1][MT];
+    mfma_tiles<1, MT, KS>(
+        a,
+        [&](int s) {
+          return as_bf16x8(in ? kb[2 * s + (lane >> 5)] : u32x4{0u, 0u, 0u, 0u});
+        },
+        acc);
+    float s = head_reduce<MT>(acc[0], wv);
+    if (lane < 32 && in && s >= tau) {
+      int slot = atomicAdd(&kept_cnt[r], 1);
+      kept_score[(int64_t)r * cap + slot] = s;
+      kept_id[(int64_t)r * cap + slot] = id;
+    }
+  }
+}
+
+// First K of (seed top-K) u (kept survivors) by (score desc, key asc).
+constexpr int kMergeThreads = 256;
+__global__ __launch_bounds__(kMergeThreads) void dosa_merge(
+    const DosaCtx* ctx, const int32_t* __restrict__ row_fb, const int32_t* __restrict__ top_idx,
+    const float* __restrict__ top_score, int topk, const float* __restrict__ kept_score,
+    const int32_t* __restrict__ kept_id, const int32_t* __restrict__ kept_cnt, int cap,
+    int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+  __shared__ uint64_t B[kMaxCapacity];
+  __shared__ uint64_t A[kMaxTopk];
+  const int r = blockIdx.x;
+  if (ctx->global_fallback || row_fb[r]) return;
+  const int m = kept_cnt[r];
+  const int P = next_pow2(m > 1 ? m : 1);
+  for (int i = threadIdx.x; i < P; i += kMergeThreads)
+    B[i] = i < m ? composite(order_key(kept_score[(int64_t)r * cap + i]),
+                             (uint32_t)kept_id[(int64_t)r * cap + i])
+                 : 0ull;
+  for (int i = threadIdx.x; i < topk; i += kMergeThreads)
+    A[i] = composite(order_key(top_score[(int64_t)r * topk + i]),
+                     (uint32_t)top_idx[(int64_t)r * topk + i]);
+  __syncthreads();
+  bitonic_sort_desc<kMergeThreads>(B, P);
+  // rank in the merged order = own index + number of the other list's items
+  // ranking ahead (composites are distinct: the lists hold distinct keys)
+  auto count_greater = [](const uint64_t* L, int n, uint64_t x) {
+    int lo = 0, hi = n;  // L descending: first index with L[i] < x
+    while (lo < hi) {
+      int mid = (lo + hi) >> 1;
+      if (L[mid] > x) lo = mid + 1;
+      else hi = mid;
+    }
+    return lo;
+  };
+  int32_t* oi = out_idx + (int64_t)r * topk;
+  float* os = out_score ? out_score + (int64_t)r * topk : nullptr;
+  for (int i = threadIdx.x; i < topk; i += kMergeThreads) {
+    int pos = i + count_greater(B, m, A[i]);
+    if (pos < topk) {
+      oi[pos] = (int32_t)comp_idx(A[i]);
+      if (os) os[pos] = key_to_float(comp_key(A[i]));
+    }
+  }
+  for (int i = threadIdx.x; i < m; i += kMergeThreads) {
+    int pos = i + count_greater(A, topk, B[i]);
+    if (pos < topk) {
+      oi[pos] = (int32_t)comp_idx(B[i]);
+      if (os) os[pos] = key_to_float(comp_key(B[i]));
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void dosa_fallback_list(DosaCtx* ctx, const int32_t* row_fb,
+                                                           int n_q, int32_t* list) {
+  __shared__ int red[1024 / 64 + 4];
+  int before = 0;
+  const int all = ctx->global_fallback;
+  for (int base = 0; base < n_q; base += 1024) {
+    int r = base + threadIdx.x;
+    int f = (r < n_q && (all || row_fb[r])) ? 1 : 0;
+    int tot;
+    int pos = before + block_excl_scan<1024>(f, red, &tot);
+    if (f) list[pos] = r;
+    before += tot;
+  }
+  if (threadIdx.x == 0) ctx->n_fallback = before;
+}
+
+__global__ void dosa_stats(const DosaCtx* ctx, const float* top_score, int topk,
+                           const int32_t* bitmap_cnt_unused, const int32_t* surv_cnt,
+                           const int32_t* row_fb, int n_q, float* tau, int32_t* n_surv,
+                           int32_t* fallback) {
+  for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < n_q; r += gridDim.x * blockDim.x) {
+    const int all = ctx->global_fallback;
+    if (tau) tau[r] = all ? __builtin_nanf("") : top_score[(int64_t)r * topk + topk - 1];
+    if (n_surv) n_surv[r] = all ? -1 : surv_cnt[r];
+    if (fallback) fallback[r] = (all || row_fb[r]) ? 1 : 0;
+  }
+}
+
+static unsigned grid_for(int64_t n, int threads) {
+  int64_t g = (n + threads - 1) / threads;
+  if (g > 65536) g = 65536;
+  return (unsigned)(g > 0 ? g : 1);
+}
+
+#define SI_TRY(expr)                                  \
+  do {                                                \
+    hipLaunchKernelGGL expr;                          \
+    hipError_t e_ = hipGetLastError();                \
+    if (e_ != hipSuccess) return e_;                  \
+  } while (0)
+
+template <int MT, int KS>
+static hipError_t run_dosa(const uint16_t* q, const uint16_t* k, const float* w, int64_t wst,
+                           const int32_t* vis, int n_q, int H, int64_t n_k, int topk,
+                           const si_dosa_params* p, int32_t* out_idx, float* out_score,
+                           const si_dosa_stats* stats, unsigned char* ws, hipStream_t st) {
+  constexpr int D = 16 * KS;
+  const DosaLayout L = dosa_layout(n_q, H, D, n_k, topk, p);
+  DosaCtx* ctx = reinterpret_cast<DosaCtx*>(ws + L.ctx);
+  auto I = [&](size_t o) { return reinterpret_cast<int32_t*>(ws + o); };
+  auto F = [&](size_t o) { return reinterpret_cast<float*>(ws + o); };
+  auto U16 = [&](size_t o) { return reinterpret_cast<uint16_t*>(ws + o); };
+  const int R = p->n_rep_queries, ns = p->n_seeds, cap = p->survivor_capacity;
+  const int64_t words = (n_k + 31) / 32;
+
+  SI_TRY((dosa_init, dim3(1), dim3(1024), 0, st, ctx, vis, n_q, n_k, ns, I(L.rep_vis), R));
+  SI_TRY((fill_i32, dim3(grid_for(n_k, 256)), dim3(256), 0, st, I(L.counts), n_k, 0));
+  SI_TRY((fill_i32, dim3(grid_for(words, 256)), dim3(256), 0, st, I(L.seed_mask), words, 0));
+  SI_TRY((fill_i32, dim3(grid_for(n_q, 256)), dim3(256), 0, st, I(L.kept_cnt), (int64_t)n_q, 0));
+  if (p->seed_ids == nullptr) {
+    SI_TRY((dosa_gather_rep, dim3(R), dim3(256), 0, st, q, w, wst, n_q, H, D, R, U16(L.rep_q),
+            F(L.rep_w)));
+    ScoreArgs sa;
+    sa.q = U16(L.rep_q); sa.q_dtype = SI_BF16; sa.k = k; sa.k_dtype = SI_BF16;
+    sa.k_scale = nullptr; sa.w = F(L.rep_w); sa.w_row_stride = H; sa.k_row_offset = nullptr;
+    sa.vis_len = I(L.rep_vis); sa.n_q = R; sa.H = H; sa.D = D; sa.n_k = n_k; sa.max_vis = n_k;
+    sa.scores = F(L.rep_scores); sa.score_stride = n_k;
+    hipError_t e = launch_score(sa, st);
+    if (e != hipSuccess) return e;
+    TopkArgs ta;
+    ta.scores = F(L.rep_scores); ta.stride = n_k; ta.vis_len = I(L.rep_vis);
+    ta.k_row_offset = nullptr; ta.n_k = n_k; ta.max_vis = n_k; ta.n_rows = R;
+    ta.K = p->rep_topk; ta.out_idx = I(L.rep_ids); ta.out_score = nullptr;
+    e = launch_topk(ta, st);
+    if (e != hipSuccess) return e;
+    SI_TRY((dosa_count, dim3(grid_for((int64_t)R * p->rep_topk, 256)), dim3(256), 0, st,
+            I(L.rep_ids), (int64_t)R * p->rep_topk, I(L.counts), n_k));
+  }
+  SI_TRY((dosa_select_seeds, dim3(1), dim3(1024), 0, st, ctx, I(L.counts), R, ns, p->seed_ids,
+          I(L.seeds), reinterpret_cast<uint32_t*>(ws + L.seed_mask)));
+  SI_TRY((dosa_gather_seed_keys, dim3(grid_for((int64_t)ns * (D / 8), 256)), dim3(256), 0, st,
+          ctx, k, I(L.seeds), ns, D, U16(L.seed_keys)));
+  constexpr int QPW = MT == 1 ? 2 : 1;
+  SI_TRY(((dosa_seed_score<MT, KS, QPW>), dim3((n_q + 4 * QPW - 1) / (4 * QPW)), dim3(256), 0, st,
+          ctx, q, U16(L.seed_keys), w, wst, n_q, H, ns, F(L.seed_scores), I(L.stat_cnt),
+          F(L.stat_sum)));
+  {
+    TopkArgs ta;
+    ta.scores = F(L.seed_scores); ta.stride = ns; ta.vis_len = nullptr; ta.k_row_offset = nullptr;
+    ta.n_k = ns; ta.max_vis = ns; ta.n_rows = n_q; ta.K = topk; ta.out_idx = I(L.top_idx);
+    ta.out_score = F(L.top_score); ta.id_map = I(L.seeds);
+    hipError_t e = launch_topk(ta, st);
+    if (e != hipSuccess) return e;
+  }
+  SI_TRY((dosa_plan, dim3(n_q), dim3(kPlanThreads), 0, st, ctx, q, w, wst, H, D, ns,
+          p->kept_heads, p->neg_active_frac, I(L.stat_cnt), F(L.stat_sum), U16(L.plan_a),
+          F(L.plan_w), F(L.plan_c)));
+  SI_TRY((dosa_knorm, dim3(grid_for(n_k, 256)), dim3(256), 0, st, k, n_k, D, F(L.knorm)));
+  SI_TRY(((dosa_bound<KS, 2>), dim3((n_q + 7) / 8), dim3(256), 0, st, ctx, U16(L.plan_a),
+          F(L.plan_w), F(L.plan_c), F(L.top_score), topk, k, F(L.knorm),
+          reinterpret_cast<const uint32_t*>(ws + L.seed_mask), vis, n_q, n_k,
+          reinterpret_cast<uint32_t*>(ws + L.bitmap), words));
+  SI_TRY((dosa_compact, dim3(n_q), dim3(kCompThreads), 0, st, ctx,
+          reinterpret_cast<const uint32_t*>(ws + L.bitmap), words, vis, n_k, cap, I(L.surv_ids),
+          I(L.surv_cnt), I(L.row_fb)));
+  SI_TRY(((dosa_rescore<MT, KS>), dim3(n_q), dim3(256), 0, st, ctx, q, w, wst, H, k, F(L.top_score),
+          topk, I(L.surv_ids), I(L.surv_cnt), I(L.row_fb), cap, F(L.kept_score), I(L.kept_id),
+          I(L.kept_cnt)));
+  SI_TRY((dosa_merge, dim3(n_q), dim3(kMergeThreads), 0, st, ctx, I(L.row_fb), I(L.top_idx),
+          F(L.top_score), topk, F(L.kept_score), I(L.kept_id), I(L.kept_cnt), cap, out_idx,
+          out_score));
+  SI_TRY((dosa_fallback_list, dim3(1), dim3(1024), 0, st, ctx, I(L.row_fb), n_q, I(L.fb_list)));
+  {
+    ScoreArgs sa;
+    sa.q = q; sa.q_dtype = SI_BF16; sa.k = k; sa.k_dtype = SI_BF16; sa.k_scale = nullptr;
+    sa.w = w; sa.w_row_stride = wst; sa.k_row_offset = nullptr; sa.vis_len = vis; sa.n_q = n_q;
+    sa.H = H; sa.D = D; sa.n_k = n_k; sa.max_vis = n_k; sa.scores = F(L.fb_scores);
+    sa.score_stride = n_k;
+    hipError_t e = launch_score_rows_listed(sa, I(L.fb_list), &ctx->n_fallback, st);
+    if (e != hipSuccess) return e;
+    TopkArgs ta;
+    ta.scores = F(L.fb_scores); ta.stride = n_k; ta.vis_len = vis; ta.k_row_offset = nullptr;
+    ta.n_k = n_k; ta.max_vis = n_k; ta.n_rows = n_q; ta.K = topk; ta.out_idx = out_idx;
+    ta.out_score = out_score; ta.row_list = I(L.fb_list); ta.row_count = &ctx->n_fallback;
+    e = launch_topk(ta, st);
+    if (e != hipSuccess) return e;
+  }
+  if (stats && (stats->tau || stats->n_survivors || stats->fallback))
+    SI_TRY((dosa_stats, dim3(grid_for(n_q, 256)), dim3(256), 0, st, ctx, F(L.top_score), topk,
+            nullptr, I(L.surv_cnt), I(L.row_fb), n_q, stats->tau, stats->n_survivors,
+            stats->fallback));
+  return hipSuccess;
+}
+
+}  // namespace si
+
+using namespace si;
+
+extern "C" size_t dosa_prune_topk_workspace(int32_t n_q, int32_t H, int32_t D, int64_t n_k,
+                                            int32_t topk, const si_dosa_params* p) {
+  if (!p || n_q < 0 || H < 1 || D < 1 || n_k < 0 || topk < 1 || p->n_rep_queries < 1 ||
+      p->n_seeds < 1 || p->rep_topk < 1 || p->survivor_capacity < 1)
+    return 0;
+  return dosa_layout(n_q, H, D, n_k, topk, p).total;
+}
+
+extern "C" si_status dosa_prune_topk(const void* q, const void* k, si_dtype dtype, const float* w,
+                                     int64_t w_row_stride, const int32_t* vis_len, int32_t n_q,
+                                     int32_t H, int32_t D, int64_t n_k, int32_t topk,
+                                     const si_dosa_params* p, int32_t* out_idx, float* out_score,
+                                     const si_dosa_stats* stats, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  if (!p || n_q < 0 || H < 1 || H > 64 || (D != 64 && D != 128) || n_k < 0 || n_k > INT32_MAX ||
+      topk < 1 || topk > kMaxTopk || w_row_stride < 0)
+    return SI_ERR_INVALID_ARGUMENT;
+  if (p->n_seeds < topk || (int64_t)p->n_seeds > n_k || p->n_rep_queries < 1 ||
+      p->n_rep_queries > kMaxRep || p->rep_topk < 1 || p->rep_topk > kMaxTopk ||
+      p->kept_heads < 0 || p->kept_heads > 31 || p->kept_heads > H ||
+      p->survivor_capacity < 1 || p->survivor_capacity > kMaxCapacity ||
+      !(p->neg_active_frac == p->neg_active_frac))
+    return SI_ERR_INVALID_ARGUMENT;
+  if (dtype != SI_BF16) return SI_ERR_UNSUPPORTED_DTYPE;
+  if (n_q == 0) return SI_OK;
+  if (!q || !k || !w || !vis_len || !out_idx) return SI_ERR_INVALID_ARGUMENT;
+  auto al = [](const void* x, uintptr_t a) { return (reinterpret_cast<uintptr_t>(x) & (a - 1)) == 0; };
+  if (!al(q, 16) || !al(k, 16) || !al(w, 4) || !al(out_idx, 4) || (out_score && !al(out_score, 4)) ||
+      (p->seed_ids && !al(p->seed_ids, 4)))
+    return SI_ERR_INVALID_ARGUMENT;
+  const size_t need = dosa_layout(n_q, H, D, n_k, topk, p).total;
+  if (!workspace || workspace_bytes < need || !al(workspace, 256)) return SI_ERR_WORKSPACE_TOO_SMALL;
+  const uint16_t* qb = reinterpret_cast<const uint16_t*>(q);
+  const uint16_t* kb = reinterpret_cast<const uint16_t*>(k);
+  unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
+  hipError_t e;
+  const bool mt1 = H <= 32;
+  if (D == 128)
+    e = mt1 ? run_dosa<1, 8>(qb, kb, w, w_row_stride, vis_len, n_q, H, n_k, topk, p, out_idx,
+                             out_score, stats, ws, stream)
+            : run_dosa<2, 8>(qb, kb, w, w_row_stride, vis_len, n_q, H, n_k, topk, p, out_idx,
+                             out_score, stats, ws, stream);
+  else
+    e = mt1 ? run_dosa<1, 4>(qb, kb, w, w_row_stride, vis_len, n_q, H, n_k, topk, p, out_idx,
+                             out_score, stats, ws, stream)
+            : run_dosa<2, 4>(qb, kb, w, w_row_stride, vis_len, n_q, H, n_k, topk, p, out_idx,
+                             out_score, stats, ws, stream);
+  return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
+}

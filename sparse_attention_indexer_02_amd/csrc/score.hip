@@ -5,76 +5,19 @@
 //  * score_mfma_shared: bf16 q and bf16 keys shared by all rows (prefill).
 //    Heads sit in the MFMA row dimension (32x32x16 bf16 tiles), keys in
 //    the column dimension, D is the reduction.  A workgroup of 4 waves owns
-//    4*QPW queries and streams 32-key tiles through LDS; each key tile is
-//    read from L2 once per workgroup and feeds every query of it.  The
-//    ReLU * w head reduction runs in registers on the accumulator tile.
+//    4*QPW queries and streams 32-key tiles through LDS (double buffered);
+//    each key tile is read from L2 once per workgroup and feeds every query
+//    of it.  The ReLU * w head reduction runs in registers on the
+//    accumulator tile.  Optionally driven by a device row list.
 //  * score_mfma_rows: bf16 queries against per-row keys (decode layout),
 //    keys bf16 or OCP fp8 e4m3fn (converted exactly to bf16 in registers,
 //    per-token scale applied after the head sum: ReLU(c x) = c ReLU(x) for
 //    c > 0).  No reuse across rows, so keys go straight to registers.
 //  * score_generic: VALU fp32 path for fp32 inputs and shapes the MFMA
 //    kernels do not cover.
-#include "si_internal.hpp"
+#include "score_micro.hpp"
 
 namespace si {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// The one score epilogue every bf16 MFMA path uses, so a (query, key) score
-// is the same bits wherever it is computed.  acc[mt] holds the 32x32 tile of
-// head rows mt*32.. for this lane's key column; lane l holds rows
-// 8*(v/4) + 4*(l/32) + v%4, v = 0..15.  Sum order: tiles, then v, then the
-// two lane halves.
-template <int MT>
-__device__ __forceinline__ float head_reduce(const f32x16 (&acc)[MT], const float (&wv)[MT][16]) {
-  float s = 0.0f;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s = __builtin_fmaf(wv[mt][v], __builtin_fmaxf(acc[mt][v], 0.0f), s);
-  float o = __shfl_xor(s, 32, 64);
-  return (threadIdx.x & 32) ? o + s : s + o;
-}
-
-// Weight fragment of this lane for head tile mt.
-template <int MT>
-__device__ __forceinline__ void load_w_frag(const float* w, int64_t w_stride, int r, int H,
-                                            bool valid, float (&wv)[MT][16]) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      int h = mt * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      wv[mt][v] = (valid && h < H) ? w[(int64_t)r * w_stride + h] : 0.0f;
-    }
-}
-
-// Query fragment: lane l supplies row h = mt*32 + l%32, k-step s covers
-// d = 16 s + 8 (l/32) + 0..7.
-template <int MT, int KS>
-__device__ __forceinline__ void load_q_frag(const uint16_t* q, int r, int H, bool valid,
-                                            bf16x8 (&a)[MT][KS]) {
-  constexpr int D = 16 * KS;
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    int h = mt * 32 + (lane & 31);
-    bool ok = valid && h < H;
-    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((int64_t)r * H + (ok ? h : 0)) * D);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4 v = ok ? src[2 * s + (lane >> 5)] : u32x4{0u, 0u, 0u, 0u};
-      a[mt][s] = as_bf16x8(v);
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Shared-key prefill kernel.
@@ -83,27 +26,43 @@ template <int MT, int KS, int QPW>
 __global__ __launch_bounds__(256, 2) void score_mfma_shared(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     int64_t w_stride, const int32_t* __restrict__ vis_len, int n_q, int H, int64_t n_k,
-    int64_t max_vis, float* __restrict__ scores, int64_t score_stride) {
+    int64_t max_vis, float* __restrict__ scores, int64_t score_stride,
+    const int32_t* __restrict__ row_list, const int32_t* __restrict__ row_count) {
   constexpr int D = 16 * KS;
   constexpr int QB = 4 * QPW;                  // queries per workgroup
   constexpr int ROWB = D * 2 + 16;             // padded LDS row: conflict-free b128 reads
-  constexpr int CHUNKS = 32 * (D * 2 / 16);    // 16-byte chunks per 32-key tile
+  constexpr int CPK = D * 2 / 16;              // 16-byte chunks per key
+  constexpr int CHUNKS = 32 * CPK;             // 16-byte chunks per 32-key tile
   constexpr int CPT = (CHUNKS + 255) / 256;    // chunks per thread
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][32 * ROWB];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n_groups = (n_q + QB - 1) / QB;
-  const int g = n_groups - 1 - (int)blockIdx.x;  // longest rows first
-  const int r0 = g * QB;
+  int n_act = n_q;
+  int g = (int)blockIdx.x;
+  if (row_list) {
+    n_act = *row_count;
+    if (g * QB >= n_act) return;
+  } else {
+    g = (n_q + QB - 1) / QB - 1 - g;  // longest rows (highest index) first
+  }
+  auto row_of = [&](int i) -> int {  // slot i of this workgroup -> row, or -1
+    int s = g * QB + i;
+    if (s >= n_act) return -1;
+    return row_list ? row_list[s] : s;
+  };
 
+  int myrow[QPW];
   int64_t vis[QPW];
   int64_t end = 0;
   for (int i = 0; i < QB; ++i) {
-    int r = r0 + i;
+    int r = row_of(i);
     int64_t off, v = 0;
-    if (r < n_q) v = visible_len(vis_len, nullptr, r, n_k, max_vis, &off);
+    if (r >= 0) v = visible_len(vis_len, nullptr, r, n_k, max_vis, &off);
     end = v > end ? v : end;
-    if (i / QPW == wave) vis[i % QPW] = v;
+    if (i / QPW == wave) {
+      vis[i % QPW] = v;
+      myrow[i % QPW] = r;
+    }
   }
   if (end == 0) return;
 
@@ -111,9 +70,8 @@ __global__ __launch_bounds__(256, 2) void score_mfma_shared(
   float wv[QPW][MT][16];
 #pragma unroll
   for (int i = 0; i < QPW; ++i) {
-    int r = r0 + wave * QPW + i;
-    load_q_frag<MT, KS>(q, r, H, r < n_q, a[i]);
-    load_w_frag<MT>(w, w_stride, r, H, r < n_q, wv[i]);
+    load_q_frag<MT, KS>(q, myrow[i], H, myrow[i] >= 0, a[i]);
+    load_w_frag<MT>(w, w_stride, myrow[i], H, myrow[i] >= 0, wv[i]);
   }
 
   const int ntiles = (int)((end + 31) / 32);
@@ -122,7 +80,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma_shared(
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       int ch = threadIdx.x + 256 * c;
-      int key = ch / (D * 2 / 16), part = ch % (D * 2 / 16);
+      int key = ch / CPK, part = ch % CPK;
       int64_t j = (int64_t)t * 32 + key;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (ch < CHUNKS && j < n_k) v = reinterpret_cast<const u32x4*>(k + j * D)[part];
@@ -133,7 +91,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma_shared(
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       int ch = threadIdx.x + 256 * c;
-      int key = ch / (D * 2 / 16), part = ch % (D * 2 / 16);
+      int key = ch / CPK, part = ch % CPK;
       if (ch < CHUNKS) *reinterpret_cast<u32x4*>(&lds[buf][key * ROWB + part * 16]) = pre[c];
     }
   };
@@ -144,29 +102,17 @@ __global__ __launch_bounds__(256, 2) void score_mfma_shared(
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < ntiles) fetch(t + 1);
-    f32x16 acc[QPW][MT];
-#pragma unroll
-    for (int i = 0; i < QPW; ++i)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][mt][v] = 0.0f;
     const unsigned char* brow = &lds[buf][(lane & 31) * ROWB + (lane >> 5) * 16];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      bf16x8 b = as_bf16x8(*reinterpret_cast<const u32x4*>(brow + 32 * s));
-#pragma unroll
-      for (int i = 0; i < QPW; ++i)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[i][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][mt][s], b, acc[i][mt], 0, 0, 0);
-    }
+    f32x16 acc[QPW][MT];
+    mfma_tiles<QPW, MT, KS>(
+        a, [&](int s) { return as_bf16x8(*reinterpret_cast<const u32x4*>(brow + 32 * s)); },
+        acc);
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
       float s = head_reduce<MT>(acc[i], wv[i]);
       int64_t j = (int64_t)t * 32 + (lane & 31);
-      int r = r0 + wave * QPW + i;
-      if (lane < 32 && r < n_q && j < vis[i]) scores[(int64_t)r * score_stride + j] = s;
+      if (lane < 32 && myrow[i] >= 0 && j < vis[i])
+        scores[(int64_t)myrow[i] * score_stride + j] = s;
     }
     if (t + 1 < ntiles) stash(buf ^ 1);
     __syncthreads();
@@ -174,17 +120,13 @@ __global__ __launch_bounds__(256, 2) void score_mfma_shared(
 }
 
 // ---------------------------------------------------------------------------
-// Per-row keys (decode layout), bf16 or fp8 keys.  Grid (chunks, rows); each
+// Per-row keys (decode layout), bf16 or fp8 keys.  Grid (rows, chunks); each
 // wave takes 32-key tiles of its row's chunk.  Lane l handles key l%32 and
 // the D-half l/32: in k-step s it supplies d = (D/2)(l/32) + 8 s + 0..7, so
 // each lane reads one contiguous half-row; the query fragments use the same
 // d order.
 // ---------------------------------------------------------------------------
 constexpr int kRowsChunk = 2048;  // keys per workgroup
-
-__device__ __forceinline__ uint32_t bf16pair(uint32_t lo16, uint32_t hi16) {
-  return (lo16 & 0xFFFFu) | (hi16 << 16);
-}
 
 template <int MT, int KS, bool FP8>
 __global__ __launch_bounds__(256, 2) void score_mfma_rows(
@@ -201,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows(
   if (c0 >= v) return;
   const int64_t c1 = (c0 + kRowsChunk < v) ? c0 + kRowsChunk : v;
 
-  bf16x8 a[MT][KS];
+  bf16x8 a[1][MT][KS];
   float wv[MT][16];
   {
     const int hf = lane >> 5;
@@ -214,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows(
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         u32x4 x = ok ? src[s] : u32x4{0u, 0u, 0u, 0u};
-        a[mt][s] = as_bf16x8(x);
+        a[0][mt][s] = as_bf16x8(x);
       }
     }
     load_w_frag<MT>(w, w_stride, r, H, true, wv);
@@ -224,11 +166,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows(
     const int64_t j = t0 + (lane & 31);
     const bool in = j < c1;
     const int64_t key = off + (in ? j : c0);
-    f32x16 acc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[mt][e] = 0.0f;
+    f32x16 acc[1][MT];
     if (FP8) {
       // D/2 fp8 bytes per lane = KS * 8 bytes.
       const uint8_t* kb = reinterpret_cast<const uint8_t*>(kv) + key * D + (lane >> 5) * (D / 2);
@@ -241,35 +179,28 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows(
         raw[4 * c + 2] = x[2];
         raw[4 * c + 3] = x[3];
       }
+      mfma_tiles<1, MT, KS>(
+          a,
+          [&](int s) {
+            u32x4 bb;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        u32x4 bb;
-#pragma unroll
-        for (int hw = 0; hw < 2; ++hw) {
-          uint32_t word = raw[2 * s + hw];
-          auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false);
-          auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true);
-          bb[2 * hw + 0] = __builtin_bit_cast(uint32_t, p0);
-          bb[2 * hw + 1] = __builtin_bit_cast(uint32_t, p1);
-        }
-        bf16x8 b = as_bf16x8(bb);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][s], b, acc[mt], 0, 0, 0);
-      }
+            for (int hw = 0; hw < 2; ++hw) {
+              uint32_t word = raw[2 * s + hw];
+              auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false);
+              auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true);
+              bb[2 * hw + 0] = __builtin_bit_cast(uint32_t, p0);
+              bb[2 * hw + 1] = __builtin_bit_cast(uint32_t, p1);
+            }
+            return as_bf16x8(bb);
+          },
+          acc);
     } else {
       const u32x4* kb = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(kv) +
                                                        key * D + (lane >> 5) * (D / 2));
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        u32x4 x = in ? kb[s] : u32x4{0u, 0u, 0u, 0u};
-        bf16x8 b = as_bf16x8(x);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][s], b, acc[mt], 0, 0, 0);
-      }
+      mfma_tiles<1, MT, KS>(
+          a, [&](int s) { return as_bf16x8(in ? kb[s] : u32x4{0u, 0u, 0u, 0u}); }, acc);
     }
-    float s = head_reduce<MT>(acc, wv);
+    float s = head_reduce<MT>(acc[0], wv);
     if (FP8) s *= (in ? kscale[key] : 0.0f);
     if (lane < 32 && in) scores[(int64_t)r * score_stride + j] = s;
   }
@@ -332,19 +263,20 @@ bool score_mfma_supported(const ScoreArgs& a) {
   if (a.q_dtype != SI_BF16) return false;
   if (a.k_dtype != SI_BF16 && a.k_dtype != SI_FP8_E4M3FN) return false;
   if (a.D != 64 && a.D != 128) return false;
-  if (a.H < 1 || a.H > 64) return false;
-  return true;
+  return a.H >= 1 && a.H <= 64;
 }
 
 template <int MT, int KS>
-static hipError_t launch_mfma(const ScoreArgs& a, hipStream_t st) {
+static hipError_t launch_mfma(const ScoreArgs& a, const int32_t* row_list,
+                              const int32_t* row_count, hipStream_t st) {
   if (a.k_row_offset == nullptr && a.k_dtype == SI_BF16) {
     constexpr int QPW = (MT == 1) ? 2 : 1;
     const int groups = (a.n_q + 4 * QPW - 1) / (4 * QPW);
     hipLaunchKernelGGL((score_mfma_shared<MT, KS, QPW>), dim3(groups), dim3(256), 0, st,
                        reinterpret_cast<const uint16_t*>(a.q),
                        reinterpret_cast<const uint16_t*>(a.k), a.w, a.w_row_stride, a.vis_len,
-                       a.n_q, a.H, a.n_k, a.max_vis, a.scores, a.score_stride);
+                       a.n_q, a.H, a.n_k, a.max_vis, a.scores, a.score_stride, row_list,
+                       row_count);
   } else {
     const int64_t chunks = (a.max_vis + kRowsChunk - 1) / kRowsChunk;
     dim3 grid((unsigned)a.n_q, (unsigned)(chunks > 0 ? chunks : 1));
@@ -366,12 +298,29 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
   if (a.n_q == 0 || a.max_vis == 0) return hipSuccess;
   if (score_mfma_supported(a)) {
     const int MT = a.H <= 32 ? 1 : 2;
-    if (a.D == 128) return MT == 1 ? launch_mfma<1, 8>(a, st) : launch_mfma<2, 8>(a, st);
-    return MT == 1 ? launch_mfma<1, 4>(a, st) : launch_mfma<2, 4>(a, st);
+    if (a.D == 128)
+      return MT == 1 ? launch_mfma<1, 8>(a, nullptr, nullptr, st)
+                     : launch_mfma<2, 8>(a, nullptr, nullptr, st);
+    return MT == 1 ? launch_mfma<1, 4>(a, nullptr, nullptr, st)
+                   : launch_mfma<2, 4>(a, nullptr, nullptr, st);
   }
   const int64_t bx = (a.max_vis + 255) / 256;
   hipLaunchKernelGGL(score_generic, dim3((unsigned)a.n_q, (unsigned)bx), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+// Shared-key bf16 scoring of the rows listed on the device (row_list[0 ..
+// *row_count)), with exactly the arithmetic of launch_score for the same
+// shapes; n_q bounds the list length.
+hipError_t launch_score_rows_listed(const ScoreArgs& a, const int32_t* row_list,
+                                    const int32_t* row_count, hipStream_t st) {
+  if (a.n_q == 0 || a.max_vis == 0) return hipSuccess;
+  const int MT = a.H <= 32 ? 1 : 2;
+  if (a.D == 128)
+    return MT == 1 ? launch_mfma<1, 8>(a, row_list, row_count, st)
+                   : launch_mfma<2, 8>(a, row_list, row_count, st);
+  return MT == 1 ? launch_mfma<1, 4>(a, row_list, row_count, st)
+                 : launch_mfma<2, 4>(a, row_list, row_count, st);
 }
 
 }  // namespace si

@@ -1,0 +1,95 @@
+// The bf16 MFMA score micro-kernel shared by every path that must produce
+// the same bits for a (query, key) score: the prefill score kernel, and
+// DoSA's seed scoring, survivor rescoring and exact fallback.
+//
+// Layout (v_mfma_f32_32x32x16_bf16): heads are MFMA rows, keys columns, D is
+// the reduction.  Lane l supplies head row mt*32 + l%32 of the query and key
+// column l%32; in k-step s both operands cover d = 16 s + 8 (l/32) + 0..7.
+// The accumulator lane l holds rows 8*(v/4) + 4*(l/32) + v%4 (v = 0..15) of
+// its key column.
+#pragma once
+
+#include "si_internal.hpp"
+
+namespace si {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Score epilogue: s = sum_h w_h max(x_h, 0) for this lane's key column.
+// Fixed order: tiles, then v, then the two lane halves - the order is part
+// of what makes a score the same bits everywhere.
+template <int MT>
+__device__ __forceinline__ float head_reduce(const f32x16 (&acc)[MT], const float (&wv)[MT][16]) {
+  float s = 0.0f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      s = __builtin_fmaf(wv[mt][v], __builtin_fmaxf(acc[mt][v], 0.0f), s);
+  float o = __shfl_xor(s, 32, 64);
+  return (threadIdx.x & 32) ? o + s : s + o;
+}
+
+// Weight fragment of this lane for head tiles mt = 0..MT-1 of row r.
+template <int MT>
+__device__ __forceinline__ void load_w_frag(const float* w, int64_t w_stride, int r, int H,
+                                            bool valid, float (&wv)[MT][16]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      int h = mt * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      wv[mt][v] = (valid && h < H) ? w[(int64_t)r * w_stride + h] : 0.0f;
+    }
+}
+
+// Query fragment of row r: head rows h = mt*32 + l%32 (zero beyond H).
+template <int MT, int KS>
+__device__ __forceinline__ void load_q_frag(const uint16_t* q, int r, int H, bool valid,
+                                            bf16x8 (&a)[MT][KS]) {
+  constexpr int D = 16 * KS;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    int h = mt * 32 + (lane & 31);
+    bool ok = valid && h < H;
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((int64_t)r * H + (ok ? h : 0)) * D);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 v = ok ? src[2 * s + (lane >> 5)] : u32x4{0u, 0u, 0u, 0u};
+      a[mt][s] = as_bf16x8(v);
+    }
+  }
+}
+
+// acc[i] = query i's head tiles x one 32-key tile, for QPW queries sharing
+// the key tile.  bfrag(s) returns this lane's 8 key elements of k-step s
+// (d = 16 s + 8 (l/32) + 0..7 of key l%32).  Each accumulator sees the same
+// MFMA sequence (k-steps in order from zero) whatever QPW is; k-step outer
+// keeps QPW * MT independent chains in flight.
+template <int QPW, int MT, int KS, class BFrag>
+__device__ __forceinline__ void mfma_tiles(const bf16x8 (&a)[QPW][MT][KS], BFrag bfrag,
+                                           f32x16 (&acc)[QPW][MT]) {
+#pragma unroll
+  for (int i = 0; i < QPW; ++i)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][mt][v] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    bf16x8 b = bfrag(s);
+#pragma unroll
+    for (int i = 0; i < QPW; ++i)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[i][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][mt][s], b, acc[i][mt], 0, 0, 0);
+  }
+}
+
+}  // namespace si

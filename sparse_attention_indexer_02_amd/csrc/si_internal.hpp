@@ -191,17 +191,21 @@ bool score_mfma_supported(const ScoreArgs& a);
 struct TopkArgs {
   const float* scores;  // row r at scores + r * stride
   int64_t stride;
-  const int32_t* vis_len;
+  const int32_t* vis_len;  // null: every row has max_vis items
   const int64_t* k_row_offset;
   int64_t n_k, max_vis;
   int32_t n_rows;
   int32_t K;
   int32_t* out_idx;     // [n_rows, K]
   float* out_score;     // [n_rows, K] or null
-  const int32_t* id_map;  // optional increasing map position -> id
+  const int32_t* id_map = nullptr;     // optional increasing map position -> id
+  const int32_t* row_list = nullptr;   // optional: only rows row_list[0 .. *row_count)
+  const int32_t* row_count = nullptr;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 constexpr int kMaxTopk = 4096;
+hipError_t launch_score_rows_listed(const ScoreArgs& a, const int32_t* row_list,
+                                    const int32_t* row_count, hipStream_t st);
 
 hipError_t launch_witness(int32_t* idx, int32_t rows, int32_t topk, const int32_t* lens,
                           int32_t S, int32_t keep, int32_t B, hipStream_t st);

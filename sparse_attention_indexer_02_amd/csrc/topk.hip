@@ -23,9 +23,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkArgs a) {
   __shared__ int red[T / 64 + 4];
   __shared__ int counter;
 
-  const int r = blockIdx.x;
+  int r = blockIdx.x;
+  if (a.row_list) {
+    if (r >= *a.row_count) return;
+    r = a.row_list[r];
+  }
   int64_t off;
-  const int64_t n = visible_len(a.vis_len, a.k_row_offset, r, a.n_k, a.max_vis, &off);
+  const int64_t n =
+      a.vis_len ? visible_len(a.vis_len, a.k_row_offset, r, a.n_k, a.max_vis, &off) : a.max_vis;
   const float* row = a.scores + (int64_t)r * a.stride;
   const int K = a.K;
   const bool staged = n <= kStage;

@@ -164,7 +164,10 @@ def test_dosa_refusals(L):
     good = DosaParams(16, 4, 8, 8, 0.5, None, 64)
     assert call(DosaParams(4, 4, 8, 8, 0.5, None, 64)) == INVALID  # n_seeds < topk
     assert call(DosaParams(16, 0, 8, 8, 0.5, None, 64)) == INVALID  # no representative rows
-    assert call(DosaParams(16, 4, 8, 17, 0.5, None, 64)) == INVALID  # kept_heads > 16
+    assert call(DosaParams(16, 4, 8, 33, 0.5, None, 64)) == INVALID  # kept_heads > H
+    assert call(DosaParams(16, 65, 8, 8, 0.5, None, 64)) == INVALID  # > 64 representatives
+    assert call(DosaParams(100, 4, 8, 8, 0.5, None, 64)) == INVALID  # n_seeds > n_k
+    assert call(DosaParams(16, 4, 8, 8, 0.5, None, 8193)) == INVALID  # capacity > 8192
     assert call(DosaParams(16, 4, 8, 8, 0.5, None, 0)) == INVALID  # capacity
     assert call(good, dtype=0) == DTYPE
     assert call(good, qq=None) == INVALID

@@ -1,0 +1,150 @@
+"""GPU parity of dosa_prune_topk: bit-identical (ids and scores) to the GPU's
+unpruned idx_score_topk on every row, and within the score tolerance of the
+oracle's plain top-K."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import dev_inputs, full_config, say
+from parity import check_topk_row
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_both(cfg, **kw):
+    import sparse_attention_indexer_02_amd as si
+    d = dev_inputs(cfg)
+    K = cfg["topk"]
+    ui, us = si.idx_score_topk(d["q"], d["k"], d["w"], d["vis_len"], K)
+    dp = cfg.get("dosa", {})
+    args = dict(n_seeds=dp.get("n_seeds", 12288), n_rep_queries=dp.get("n_rep_queries", 4),
+                rep_topk=dp.get("rep_topk", 2048), kept_heads=dp.get("kept_heads", 16),
+                neg_active_frac=dp.get("neg_active_frac", 0.5))
+    args.update(kw)
+    di, ds, st = si.dosa_prune_topk(d["q"], d["k"], d["w"], d["vis_len"], K, want_stats=True,
+                                    **args)
+    torch.cuda.synchronize()
+    st = {k: v.cpu().numpy() for k, v in st.items()}
+    return ui.cpu().numpy(), us.cpu().numpy(), di.cpu().numpy(), ds.cpu().numpy(), st
+
+
+def _assert_bit_exact(ui, us, di, ds):
+    np.testing.assert_array_equal(di, ui)
+    np.testing.assert_array_equal(ds.view(np.uint32), us.view(np.uint32))
+
+
+def _oracle_rows(orc, cfg, gi, gs, rows):
+    kp = orc.problem(cfg)
+    _, _, S, M, N = orc.idx_score_topk_rows(kp, rows, want_rows=True)
+    for n, r in enumerate(rows):
+        v = orc.visible(kp, int(r))
+        check_topk_row(gi[r], gs[r], S[n, :v], M[n, :v], N[n, :v], cfg["topk"], f"dosa row {r}")
+
+
+def _small(structured, seed, n_q=48, L=700, H=32, D=128, K=64, n_seeds=256, kept=16, R=4):
+    gen = synth.dosa_structured if structured else synth.dosa
+    return gen(seed=seed, n_q=n_q, L=L, H=H, D=D, topk=K, n_seeds=n_seeds, n_rep=R, rep_topk=K,
+               kept_heads=kept)
+
+
+@pytest.mark.parametrize("structured", [False, True])
+@pytest.mark.parametrize("H,D", [(32, 128), (64, 128), (32, 64), (20, 128)])
+def test_small_equals_unpruned(orc, structured, H, D):
+    cfg = _small(structured, seed=H + D, H=H, D=D, kept=min(16, H - 1))
+    say(f"dosa small structured={structured} H={H} D={D}")
+    ui, us, di, ds, st = _run_both(cfg)
+    _assert_bit_exact(ui, us, di, ds)
+    assert np.all(st["fallback"] == 0)
+    _oracle_rows(orc, cfg, di, ds, list(range(cfg["n_q"])))
+    if structured:
+        scanned = cfg["vis_len"] - cfg["dosa"]["n_seeds"]
+        assert np.all(st["n_survivors"] <= scanned)
+        assert st["n_survivors"].sum() < scanned.sum(), "the bound pruned nothing"
+
+
+def test_integer_ties(orc):
+    """Integer-valued inputs: exact scores, many ties, ties exactly at tau."""
+    rng = np.random.default_rng(21)
+    n_q, L, H, D, K = 40, 400, 32, 128, 48
+    q = rng.integers(-2, 3, (n_q, H, D)).astype(np.float32)
+    q[:, 8:] = q[:, :8].repeat(3, axis=1)[:, :H - 8]  # reusable heads
+    k = rng.integers(-2, 3, (L, D)).astype(np.float32)
+    k[rng.random((L, D)) < 0.8] = 0
+    w = rng.choice([-1.0, -0.5, 0.5, 1.0], (n_q, H)).astype(np.float32)
+    cfg = dict(name="dosa-int", q=synth.f32_to_bf16_bits(q), q_dtype=synth.BF16,
+               k=synth.f32_to_bf16_bits(k), k_dtype=synth.BF16, k_scale=None, w=w,
+               k_row_offset=None, vis_len=(L - n_q + 1 + np.arange(n_q)).astype(np.int32),
+               n_q=n_q, H=H, D=D, n_k=L, max_vis=L, topk=K,
+               dosa=dict(n_seeds=120, n_rep_queries=3, rep_topk=K, kept_heads=8,
+                         neg_active_frac=0.5))
+    say("dosa integer ties")
+    ui, us, di, ds, st = _run_both(cfg)
+    _assert_bit_exact(ui, us, di, ds)
+    kp = orc.problem(cfg)
+    oi, os_ = orc.idx_score_topk_rows(kp, list(range(n_q)))
+    np.testing.assert_array_equal(di, oi)
+    np.testing.assert_array_equal(ds.astype(np.float64), os_)
+
+
+def test_capacity_overflow_takes_exact_path():
+    cfg = _small(False, seed=5)
+    say("dosa overflow")
+    ui, us, di, ds, st = _run_both(cfg, survivor_capacity=1)
+    _assert_bit_exact(ui, us, di, ds)
+    assert st["fallback"].sum() > 0
+
+
+def test_too_few_common_keys_falls_back():
+    cfg = _small(True, seed=6)
+    cfg["vis_len"] = cfg["vis_len"].copy()
+    cfg["vis_len"][3] = 100  # common prefix 100 < n_seeds
+    say("dosa global fallback")
+    ui, us, di, ds, st = _run_both(cfg)
+    _assert_bit_exact(ui, us, di, ds)
+    assert np.all(st["fallback"] == 1)
+
+
+def test_caller_prior():
+    """seed_ids supplied by the caller (the prior hook); an invalid prior
+    (not increasing) sends every row to the exact path."""
+    cfg = _small(True, seed=7)
+    c = int(cfg["vis_len"].min())
+    seeds = np.sort(np.random.default_rng(8).choice(c, 256, replace=False)).astype(np.int32)
+    say("dosa caller prior")
+    ui, us, di, ds, st = _run_both(cfg, seed_ids=torch.from_numpy(seeds).cuda())
+    _assert_bit_exact(ui, us, di, ds)
+    assert np.all(st["fallback"] == 0)
+    bad = seeds[::-1].copy()
+    ui, us, di, ds, st = _run_both(cfg, seed_ids=torch.from_numpy(bad).cuda())
+    _assert_bit_exact(ui, us, di, ds)
+    assert np.all(st["fallback"] == 1)
+
+
+def test_shared_weights_and_short_rows(orc):
+    cfg = _small(True, seed=9, n_q=20, L=300, n_seeds=100, K=40)
+    cfg["w"] = np.ascontiguousarray(cfg["w"][0])
+    say("dosa shared weights")
+    import sparse_attention_indexer_02_amd as si
+    d = dev_inputs(cfg)
+    ui, us = si.idx_score_topk(d["q"], d["k"], d["w"], d["vis_len"], 40)
+    di, ds, _ = si.dosa_prune_topk(d["q"], d["k"], d["w"], d["vis_len"], 40, n_seeds=100,
+                                   n_rep_queries=2, rep_topk=40, kept_heads=8)
+    torch.cuda.synchronize()
+    _assert_bit_exact(ui.cpu().numpy(), us.cpu().numpy(), di.cpu().numpy(), ds.cpu().numpy())
+
+
+@pytest.mark.parametrize("name", ["dosa", "dosa_structured"])
+def test_full_size(orc, name):
+    """4096 queries x 32768 causal keys, H32 D128 K2048, 12,288 cold-prior
+    seeds, 16 kept heads: every row bit-identical to the unpruned top-K;
+    sampled rows against the oracle."""
+    cfg = full_config(name)
+    say(f"dosa full size {name}")
+    ui, us, di, ds, st = _run_both(cfg)
+    _assert_bit_exact(ui, us, di, ds)
+    rows = [0, 1, 2047, 4094, 4095]
+    _oracle_rows(orc, cfg, di, ds, rows)
+    scanned = (cfg["vis_len"] - cfg["dosa"]["n_seeds"]).sum()
+    say(f"{name}: survivors {st['n_survivors'].clip(0).sum()} / scanned {scanned}, "
+        f"fallback rows {st['fallback'].sum()}")
