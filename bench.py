@@ -262,6 +262,86 @@ def bench_block(args):
     return out_d
 
 
+def bench_dosa(args):
+    """DoSA certified prune on the 4096 x 32768 causal chunk (H32 D128 K2048,
+    12,288 cold-prior seeds, 16 kept heads) next to the unpruned top-K of the
+    same inputs; value = visible pairs whose top-K membership is decided per
+    second (the unpruned-equivalent throughput)."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_indexer_02_amd as si
+    import synth
+    log(f"generating {args.workload} inputs")
+    cfg = synth.dosa() if args.workload == "dosa" else synth.dosa_structured()
+    d = to_device(cfg)
+    n_q, H, D, K, n_k = cfg["n_q"], cfg["H"], cfg["D"], cfg["topk"], cfg["n_k"]
+    dp = cfg["dosa"]
+    dev = d["q"].device
+    cap = 8192
+    out_i = torch.empty((n_q, K), dtype=torch.int32, device=dev)
+    out_s = torch.empty((n_q, K), dtype=torch.float32, device=dev)
+    ref_i = torch.empty_like(out_i)
+    ref_s = torch.empty_like(out_s)
+    p = si._binding.DosaParams(dp["n_seeds"], dp["n_rep_queries"], dp["rep_topk"],
+                               dp["kept_heads"], dp["neg_active_frac"], None, cap)
+    import ctypes
+    ws = torch.empty(si.lib().dosa_prune_topk_workspace(n_q, H, D, n_k, K, ctypes.byref(p)),
+                     dtype=torch.uint8, device=dev)
+    ws_u = torch.empty(si.lib().idx_score_topk_workspace(n_q, H, D, n_k, K), dtype=torch.uint8,
+                       device=dev)
+    stats = {}
+
+    def dosa():
+        _, _, st = si.dosa_prune_topk(d["q"], d["k"], d["w"], d["vis_len"], K,
+                                      n_seeds=dp["n_seeds"], n_rep_queries=dp["n_rep_queries"],
+                                      rep_topk=dp["rep_topk"], kept_heads=dp["kept_heads"],
+                                      neg_active_frac=dp["neg_active_frac"],
+                                      survivor_capacity=cap, out_idx=out_i, out_score=out_s,
+                                      want_stats=True, workspace=ws)
+        stats.update(st)
+
+    def unpruned():
+        si.idx_score_topk(d["q"], d["k"], d["w"], d["vis_len"], K, out_idx=ref_i,
+                          out_score=ref_s, workspace=ws_u)
+
+    pairs = int(cfg["vis_len"].astype(np.int64).sum())
+    wall_ms, per = timed_steps([("dosa", dosa)], args.steps, args.warmup)
+    _, per_u = timed_steps([("unpruned", unpruned)], args.steps, args.warmup)
+    torch.cuda.synchronize()
+    equal = bool(torch.equal(out_i, ref_i) and torch.equal(out_s.view(torch.int32),
+                                                            ref_s.view(torch.int32)))
+    surv = stats["n_survivors"].cpu().numpy().astype(np.int64)
+    fb = stats["fallback"].cpu().numpy()
+    scanned = int((cfg["vis_len"].astype(np.int64) - dp["n_seeds"]).sum())
+    kept = dp["kept_heads"]
+    head_dots = (n_q * dp["n_seeds"] * H + scanned * (kept + 1) +
+                 int(surv.clip(0).sum()) * H)
+    # MFMA work actually issued: seeds and survivors at H rows (32-row tiles),
+    # the bound at one 32-row tile per query
+    rows_tile = 32 * ((H + 31) // 32)
+    mfma_flops = 2.0 * D * (n_q * dp["n_seeds"] * rows_tile + pairs * 32 +
+                            int(surv.clip(0).sum()) * rows_tile)
+    ach = mfma_flops / per["dosa"] / 1e9
+    out = dict(metric=METRIC, value=pairs / (wall_ms / 1e3), unit="pairs/s", n_gpus=1,
+               steps=args.steps, warmup=args.warmup, ms_per_step=wall_ms, higher_is_better=True,
+               scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+               config=dict(workload=f"DoSA prefill {n_q}x{n_k} causal H{H} D{D} K{K}, "
+                                    f"{dp['n_seeds']} cold-prior seeds, {kept} kept heads"
+                                    f"{' (structured heads)' if 'structured' in args.workload else ''}",
+                           pairs_per_step=pairs),
+               roofline=dict(bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                             frac=ach / PEAK_BF16_TFLOPS, traffic=None,
+                             kernel="dosa_prune_topk (all kernels; MFMA flops issued)"),
+               dosa=dict(ms=per["dosa"], unpruned_ms=per_u["unpruned"],
+                         speedup_vs_unpruned=per_u["unpruned"] / per["dosa"],
+                         bit_identical_to_unpruned=equal,
+                         survival=float(surv.clip(0).sum()) / max(scanned, 1),
+                         fallback_rows=int(fb.sum()), head_dots=head_dots,
+                         dense_head_dots=pairs * H))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)

@@ -1,0 +1,65 @@
+"""GPU top-K stage (rows_topk) on given f32 score rows: ids and scores must
+equal the oracle's (score desc, id asc) top-K exactly - the scores are
+inputs, so there is no tolerance."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(kind, rng, n_rows, L):
+    if kind == "normal":
+        return rng.standard_normal((n_rows, L)).astype(np.float32) * 30
+    if kind == "equal":
+        return np.full((n_rows, L), 3.5, np.float32)
+    if kind == "few_values":
+        return rng.integers(-3, 4, (n_rows, L)).astype(np.float32)
+    if kind == "narrow":  # thousands of items share the top 11 key bits
+        return (100.0 + rng.random((n_rows, L)) * 0.01).astype(np.float32)
+    if kind == "signed_zero":
+        x = rng.choice(np.array([0.0, -0.0, 1.0, -1.0], np.float32), (n_rows, L))
+        return x.astype(np.float32)
+    if kind == "wide":
+        return (rng.standard_normal((n_rows, L)) *
+                np.exp(rng.uniform(-20, 20, (n_rows, L)))).astype(np.float32)
+    raise ValueError(kind)
+
+
+def _check(orc, scores, vis, K):
+    import sparse_attention_indexer_02_amd as si
+    st = torch.from_numpy(scores).cuda()
+    vt = torch.from_numpy(vis.astype(np.int32)).cuda()
+    gi, gs = si.rows_topk(st, vt, K)
+    torch.cuda.synchronize()
+    gi, gs = gi.cpu().numpy(), gs.cpu().numpy()
+    for r in range(scores.shape[0]):
+        v = int(min(max(vis[r], 0), scores.shape[1]))
+        oi, os_, _ = orc.topk(scores[r, :v].astype(np.float64), K)
+        np.testing.assert_array_equal(gi[r], oi, err_msg=f"row {r} n={v} K={K}")
+        np.testing.assert_array_equal(gs[r].astype(np.float64), os_, err_msg=f"row {r}")
+
+
+@pytest.mark.parametrize("kind", ["normal", "equal", "few_values", "narrow", "signed_zero", "wide"])
+@pytest.mark.parametrize("L,K", [(8192, 2048), (5000, 2048), (3000, 100), (8192, 1), (700, 513)])
+def test_short_rows(orc, kind, L, K):
+    rng = np.random.default_rng(L + K)
+    n_rows = 24
+    scores = _rows(kind, rng, n_rows, L)
+    vis = rng.integers(0, L + 1, n_rows)
+    vis[:4] = [0, 1, min(K, L), L]
+    say(f"topk {kind} L={L} K={K}")
+    _check(orc, scores, vis, K)
+
+
+@pytest.mark.parametrize("kind", ["normal", "few_values"])
+def test_long_rows(orc, kind):
+    """Rows longer than the register-resident path (up to 40000)."""
+    rng = np.random.default_rng(3)
+    scores = _rows(kind, rng, 6, 40000)
+    vis = np.array([40000, 8193, 12288, 20000, 2, 0])
+    say(f"topk long {kind}")
+    _check(orc, scores, vis, 2048)
+    _check(orc, scores, vis, 4096)
