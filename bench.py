@@ -35,18 +35,20 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def counters_for(kernel_file, workload):
-    """HBM traffic per launch measured with rocprofv3 PMC counters, if the
-    summary in profiles/ was taken on the kernel source as it is now."""
+def counters_for(workload):
+    """HBM bytes per launch of the workload's dominant kernel, measured with
+    rocprofv3 FETCH_SIZE / WRITE_SIZE and scaled against a plain copy, if that
+    measurement was taken on the kernel sources as they are now (else None)."""
     path = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(path):
         return None
     try:
-        data = json.load(open(path))
-        ent = data[workload]
-        src = open(os.path.join(ROOT, "sparse_attention_indexer_02_amd", "csrc", kernel_file),
-                   "rb").read()
-        if ent["source_sha256"] != hashlib.sha256(src).hexdigest():
+        ent = json.load(open(path))[workload]
+        h = hashlib.sha256()
+        for f in ent["sources"]:
+            h.update(open(os.path.join(ROOT, "sparse_attention_indexer_02_amd", "csrc", f),
+                          "rb").read())
+        if ent["source_sha256"] != h.hexdigest():
             return None
         return ent["hbm_bytes_per_launch"]
     except (KeyError, ValueError, OSError):
@@ -171,12 +173,12 @@ def bench_indexer(args, cfg, workload):
         # per-row keys: every key byte is read once; HBM-bound
         ach = score_bytes / per["score"] / 1e6
         roof = dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=ach / PEAK_HBM_GBS, traffic=counters_for("score.hip", workload),
+                    frac=ach / PEAK_HBM_GBS, traffic=counters_for(workload),
                     kernel="score_mfma_rows")
     else:
         ach = kern["score"]["tflops"]
         roof = dict(bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=ach / PEAK_BF16_TFLOPS, traffic=counters_for("score.hip", workload),
+                    frac=ach / PEAK_BF16_TFLOPS, traffic=counters_for(workload),
                     kernel="score_mfma_shared")
     step_ms = per["score"] + per["topk"] + per["witness"]
     out = dict(metric=METRIC, value=pairs / (wall_ms / 1e3), unit="pairs/s", n_gpus=1,
@@ -241,7 +243,7 @@ def bench_block(args):
                                       f"block {bs}, top {cfg['top_blocks']}"),
                  roofline=dict(bound="alu", achieved=ach, peak=PEAK_VALU_TOPS, unit="TFLOP/s",
                                frac=ach / PEAK_VALU_TOPS,
-                               traffic=counters_for("block_select.hip", "block"),
+                               traffic=counters_for("block"),
                                kernel="block_max"))
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -351,17 +353,28 @@ def main():
                     choices=["prefill", "decode", "dosa", "dosa_structured", "block"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run a plain device-to-device copy of this many MiB (outside "
+                         "the timed region) so HBM byte counters can be scaled against it")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps(dict(metric=METRIC, error="this build measures one GPU; multi-GPU "
-                              "row/key sharding is described in DESIGN.md and not run",
+        print(json.dumps(dict(metric=METRIC, error="only one GPU is measured: the path runs "
+                              "on a single device and no multi-GPU sharding is implemented",
                               n_gpus=args.gpus)))
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read, {n} bytes written")
+        del src, dst
     import synth
     if args.workload == "block":
         out = bench_block(args)
