@@ -162,7 +162,8 @@ si_status rows_topk(const float* scores, int64_t score_stride, const int32_t* vi
  *        the row took the exact path).
  * Rows fall back to the exact path as a whole when fewer than n_seeds keys
  * are visible to every row.
- * Errors: as idx_score_topk, plus INVALID_ARGUMENT for params out of range.
+ * Errors: as idx_score_topk, plus INVALID_ARGUMENT for params out of range
+ * and for key matrices of 2^31 bytes or more (n_k * D * 2 > INT32_MAX).
  * ------------------------------------------------------------------------ */
 typedef struct {
   int32_t n_seeds;

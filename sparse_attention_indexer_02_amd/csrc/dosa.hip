@@ -873,8 +873,8 @@ extern "C" si_status dosa_prune_topk(const void* q, const void* k, si_dtype dtyp
                                      const si_dosa_params* p, int32_t* out_idx, float* out_score,
                                      const si_dosa_stats* stats, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream) {
-  if (!p || n_q < 0 || H < 1 || H > 64 || (D != 64 && D != 128) || n_k < 0 || n_k > INT32_MAX ||
-      topk < 1 || topk > kMaxTopk || w_row_stride < 0)
+  if (!p || n_q < 0 || H < 1 || H > 64 || (D != 64 && D != 128) || n_k < 0 ||
+      n_k * D * 2 > INT32_MAX || topk < 1 || topk > kMaxTopk || w_row_stride < 0)
     return SI_ERR_INVALID_ARGUMENT;
   if (p->n_seeds < topk || (int64_t)p->n_seeds > n_k || p->n_rep_queries < 1 ||
       p->n_rep_queries > kMaxRep || p->rep_topk < 1 || p->rep_topk > kMaxTopk ||

@@ -19,6 +19,11 @@
 
 namespace si {
 
+// Word 3 of a raw gfx9-family buffer resource: 32-bit data format, no
+// swizzle, no index stride; with stride 0 the hardware range-checks the
+// byte offset against num_records.
+constexpr int kBufWord3 = 0x00020000;
+
 // ---------------------------------------------------------------------------
 // Shared-key prefill kernel.
 // ---------------------------------------------------------------------------
@@ -76,45 +81,59 @@ __global__ __launch_bounds__(256, 2) void score_mfma_shared(
 
   const int ntiles = (int)((end + 31) / 32);
   u32x4 pre[CPT];
+  static_assert(CHUNKS % 256 == 0, "every thread stages whole chunks");
+  // Keys and score rows go through buffer resources: 32-bit offsets (one
+  // VALU op per address) and the hardware range check, which returns zero
+  // for a key load past n_k and drops a score store past the row's visible
+  // length, so no load or store sits under a branch and the compiler keeps
+  // every memory wait out of the MFMA section.  The launcher guarantees
+  // n_k * D * 2 < 2^31.
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)k, (short)0, (int)(n_k * D * 2), kBufWord3);
+  __amdgpu_buffer_rsrc_t srs[QPW];
+#pragma unroll
+  for (int i = 0; i < QPW; ++i)
+    srs[i] = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(scores + (int64_t)(myrow[i] >= 0 ? myrow[i] : 0) * score_stride), (short)0,
+        (int)(myrow[i] >= 0 ? vis[i] * 4 : 0), kBufWord3);
   auto fetch = [&](int t) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      int ch = threadIdx.x + 256 * c;
-      int key = ch / CPK, part = ch % CPK;
-      int64_t j = (int64_t)t * 32 + key;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ch < CHUNKS && j < n_k) v = reinterpret_cast<const u32x4*>(k + j * D)[part];
-      pre[c] = v;
-    }
+    for (int c = 0; c < CPT; ++c)
+      pre[c] = __builtin_amdgcn_raw_buffer_load_b128(krs, t * (32 * D * 2) + (threadIdx.x + 256 * c) * 16,
+                                                     0, 0);
   };
   auto stash = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      int ch = threadIdx.x + 256 * c;
-      int key = ch / CPK, part = ch % CPK;
-      if (ch < CHUNKS) *reinterpret_cast<u32x4*>(&lds[buf][key * ROWB + part * 16]) = pre[c];
+      const int ch = threadIdx.x + 256 * c;
+      const int key = ch / CPK, part = ch % CPK;
+      *reinterpret_cast<u32x4*>(&lds[buf][key * ROWB + part * 16]) = pre[c];
     }
   };
+  const unsigned char* lrow = &lds[0][(lane & 31) * ROWB + (lane >> 5) * 16];
 
   fetch(0);
   stash(0);
+  wait_memory();
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) fetch(t + 1);
-    const unsigned char* brow = &lds[buf][(lane & 31) * ROWB + (lane >> 5) * 16];
+    fetch(t + 1 < ntiles ? t + 1 : t);  // the last one is a harmless repeat
+    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
+    const unsigned char* brow = lrow + (t & 1) * (32 * ROWB);
     f32x16 acc[QPW][MT];
     mfma_tiles<QPW, MT, KS>(
         a, [&](int s) { return as_bf16x8(*reinterpret_cast<const u32x4*>(brow + 32 * s)); },
         acc);
+    float sc[QPW];
 #pragma unroll
-    for (int i = 0; i < QPW; ++i) {
-      float s = head_reduce<MT>(acc[i], wv[i]);
-      int64_t j = (int64_t)t * 32 + (lane & 31);
-      if (lane < 32 && myrow[i] >= 0 && j < vis[i])
-        scores[(int64_t)myrow[i] * score_stride + j] = s;
-    }
-    if (t + 1 < ntiles) stash(buf ^ 1);
+    for (int i = 0; i < QPW; ++i) sc[i] = head_reduce<MT>(acc[i], wv[i]);
+    // buffer (t + 1) & 1 held tile t - 1, read before the previous barrier
+    stash((t + 1) & 1);
+    // lanes 32-63 hold the same sums; their out-of-range offset drops them
+    const int off = lane < 32 ? (t * 32 + lane) * 4 : INT32_MAX;
+#pragma unroll
+    for (int i = 0; i < QPW; ++i)
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc[i]), srs[i], off, 0, 0);
     __syncthreads();
   }
 }
@@ -269,7 +288,13 @@ bool score_mfma_supported(const ScoreArgs& a) {
 template <int MT, int KS>
 static hipError_t launch_mfma(const ScoreArgs& a, const int32_t* row_list,
                               const int32_t* row_count, hipStream_t st) {
-  if (a.k_row_offset == nullptr && a.k_dtype == SI_BF16) {
+  // shared bf16 keys small enough for 32-bit buffer offsets go through the
+  // LDS-sharing kernel; listed rows exist only on that path
+  const bool shared = a.k_row_offset == nullptr && a.k_dtype == SI_BF16 &&
+                      a.n_k * a.D * 2 <= (int64_t)INT32_MAX &&
+                      a.max_vis * 4 <= (int64_t)INT32_MAX;
+  if (row_list != nullptr && !shared) return hipErrorInvalidValue;
+  if (shared) {
     constexpr int QPW = (MT == 1) ? 2 : 1;
     const int groups = (a.n_q + 4 * QPW - 1) / (4 * QPW);
     hipLaunchKernelGGL((score_mfma_shared<MT, KS, QPW>), dim3(groups), dim3(256), 0, st,

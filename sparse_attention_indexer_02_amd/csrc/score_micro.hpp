@@ -19,19 +19,43 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// max(x, 0) as one integer max on the bit pattern: every float with the sign
+// bit set (negatives and -0) is a negative int32 and becomes +0.  Equal in
+// value to fmaxf(x, 0) for every non-NaN x, without the NaN-quieting
+// canonicalisation the IEEE-mode fmaxf costs.
+__device__ __forceinline__ float relu(float x) {
+  const int b = __builtin_bit_cast(int, x);
+  return __builtin_bit_cast(float, b > 0 ? b : 0);
+}
+
+// Waits for every outstanding memory operation of this wave.  Placed
+// unconditionally before a key loop, it tells the compiler that the
+// prologue's fragment loads have landed, so no wait on them (nor on the
+// loop's own prefetch) is placed inside the loop.
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
 // Score epilogue: s = sum_h w_h max(x_h, 0) for this lane's key column.
-// Fixed order: tiles, then v, then the two lane halves - the order is part
-// of what makes a score the same bits everywhere.
+// Fixed order: the fma chain runs over e = mt * 16 + v in increasing e, then
+// lanes 0-31's partial is added to lanes 32-63's.  The order is part of what
+// makes a score the same bits everywhere; head_chain lets a caller split the
+// chain into pieces (interleaved with other work) without changing it.
+template <int MT>
+__device__ __forceinline__ void head_chain(const f32x16 (&acc)[MT], const float (&wv)[MT][16],
+                                           int e0, int e1, float& s) {
+#pragma unroll
+  for (int e = e0; e < e1; ++e) s = __builtin_fmaf(wv[e / 16][e % 16], relu(acc[e / 16][e % 16]), s);
+}
+
+__device__ __forceinline__ float halves_sum(float s) {
+  float o = __shfl_xor(s, 32, 64);
+  return (threadIdx.x & 32) ? o + s : s + o;
+}
+
 template <int MT>
 __device__ __forceinline__ float head_reduce(const f32x16 (&acc)[MT], const float (&wv)[MT][16]) {
   float s = 0.0f;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int v = 0; v < 16; ++v)
-      s = __builtin_fmaf(wv[mt][v], __builtin_fmaxf(acc[mt][v], 0.0f), s);
-  float o = __shfl_xor(s, 32, 64);
-  return (threadIdx.x & 32) ? o + s : s + o;
+  head_chain<MT>(acc, wv, 0, 16 * MT, s);
+  return halves_sum(s);
 }
 
 // Weight fragment of this lane for head tiles mt = 0..MT-1 of row r.
