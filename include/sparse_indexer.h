@@ -25,7 +25,9 @@
  *  - Index outputs are row-relative int32, padded with -1.
  *  - Ordering: "top-K" always means the first min(K, n) items under the
  *    total order (score descending, index ascending), -0 == +0; this one
- *    order makes tied ids reproducible everywhere.
+ *    order makes tied ids reproducible everywhere.  A NaN score (outside
+ *    the contract) ranks and is reported as -inf; no input bits make a
+ *    selection kernel read or write out of bounds.
  */
 #ifndef SPARSE_INDEXER_H
 #define SPARSE_INDEXER_H

@@ -252,7 +252,14 @@ __global__ __launch_bounds__(256, 2) void dosa_seed_score(
   constexpr int CHUNKS = 32 * CPK;
   constexpr int CPT = (CHUNKS + 255) / 256;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][32 * ROWB];
-  if (ctx->global_fallback) return;
+  if (ctx->global_fallback) {  // rows take the exact path; keep the buffer defined
+    for (int i = 0; i < 4 * QPW; ++i) {
+      const int r = (int)blockIdx.x * 4 * QPW + i;
+      if (r < n_q)
+        for (int j = threadIdx.x; j < n_seeds; j += 256) seed_scores[(int64_t)r * n_seeds + j] = 0.0f;
+    }
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r0 = (int)blockIdx.x * 4 * QPW + wave * QPW;
 

@@ -54,15 +54,13 @@ __device__ __forceinline__ int64_t visible_len(const int32_t* vis_len, const int
 // ---------------------------------------------------------------------------
 // Block-wide helpers (blockDim.x == THREADS, multiple of 64).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
+// Wavefront scan and reductions from the ROCm device library (DPP row
+// shifts and broadcasts; every lane of the wave must be active).
+extern "C" __device__ int __ockl_wfscan_add_i32(int, bool);
+extern "C" __device__ unsigned __ockl_wfred_max_u32(unsigned);
+extern "C" __device__ unsigned __ockl_wfred_min_u32(unsigned);
+
+__device__ __forceinline__ int wave_incl_scan(int x) { return __ockl_wfscan_add_i32(x, true); }
 
 // Exclusive prefix sum over the block; returns the thread's exclusive
 // prefix, *total gets the block total.  `scratch` needs THREADS/64 ints.

@@ -3,10 +3,8 @@
 // reproducible; the final selection is by full score).
 //
 // Two kernels:
-//  * topk_wave<PER>: rows of at most 64*PER scores (<= 8192), K <= 2048.
-//    One wavefront per row and no cross-wave synchronisation: the row
-//    lives in registers, every row-wide step is one pass over them, and
-//    ordered compaction is a ballot prefix.  See the kernel for the steps.
+//  * topk_block: rows of at most 8192 scores, K <= 2048, one workgroup per
+//    row holding the row in registers (see the kernel for the steps).
 //  * topk_rows: any length and K <= 4096 (long decode rows, DoSA's seed and
 //    fallback rows).  One 512-thread workgroup per row; rows up to 8192
 //    scores are staged in LDS, longer ones re-read per pass; a 3-pass radix
@@ -92,67 +90,59 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkArgs a) {
 // ---------------------------------------------------------------------------
 // Rows of at most 8192 scores, K <= 2048: one 256-thread workgroup per row,
 // thread t owning positions [32 t, 32 t + 32) in registers (16-byte loads),
-// so index order is thread order and every ordered step is one block scan.
-//  A. load, make orderable keys, histogram their top 11 bits (coarse bins,
-//     4 replicas of 16-bit counters against atomic contention), row range;
-//  B. scan of the coarse bins from the top: bin b1 holds the K-th item; the
-//     coarse counts become packed (offset << 16 | selected count) per bin;
-//  C. list bin b1's keys and refine on the list with the next 11 and 10
-//     bits: the exact K-th key T, the count above it and the ties at it (a
-//     crowded b1 refines over the registers instead);
-//  D. index-ordered compaction: keys > T, then the lowest-index keys == T;
-//  E. bucket rank: each coarse bin owns as many buckets as it has selected
-//     items, spread linearly over its low 21 key bits (~1 item per bucket
-//     for any smooth score density); an item's output slot is its bucket's
-//     offset plus the number of same-bucket items ahead of it under
-//     (score desc, index asc).
+// so index order is thread order.
+//  A. load (a NaN score is taken as -inf) and the row's value range;
+//  B. histogram over 4096 bins linear in score value over [vmin, vmax];
+//  C. scan from the top bin: the bin b1 holding the K-th item, and per bin
+//     the packed (output offset << 16 | selected count);
+//  D. the exact K-th value T inside b1: every b1 item counts the b1 items
+//     above it when b1 is small, else a radix select on the key bits of
+//     b1's items picks T;
+//  E. the selected items (> T, then the lowest-index ones == T) are
+//     scattered grouped by bin; an item's output slot is its bin's offset
+//     plus the number of same-bin items ahead of it under (score desc,
+//     index asc).  The ordered row is staged in LDS and written coalesced.
+//     If some bin holds more than kCrowd selected items (heavy ties, very
+//     uneven scores) the row is ordered by a bitonic sort instead.
 // ---------------------------------------------------------------------------
 constexpr int kBT = 256;             // threads per row
 constexpr int kBPer = 32;            // positions per thread
 constexpr int kBN = kBT * kBPer;     // 8192
 constexpr int kBK = 2048;            // largest K
-constexpr int kBItems = kBK / kBT;   // 8 dense items per thread
+constexpr int kBItems = kBK / kBT;   // ordered items per thread
+constexpr int kBins = 4096;          // value bins
+constexpr int kBinsPer = kBins / kBT;
+constexpr int kBrute = 256;          // largest b1 ranked item by item
+constexpr int kCrowd = 64;           // largest per-bin count ranked by scanning the bin
 
-struct BlockSmem {
-  // coarse histogram: 4 replicas x 2048 16-bit counters; afterwards words
-  // [0, 2048) hold the packed per-bin (offset << 16 | count) and words
-  // [2048, 4096) the bucket counters/offsets
-  uint32_t coarse[4096];
-  // candidate list + refine histogram, then the dense list, then buckets
+struct alignas(16) BlockSmem {
+  uint32_t bins[kBins];  // histogram, then packed (cursor << 16 | selected count)
   union {
-    struct {
-      uint32_t list[2048];
-      uint32_t rh[2048];
-    } r;
-    uint64_t dense[kBK];
+    uint64_t comp[kBK];     // selected (key << 32 | ~position) grouped by bin,
+                            // then the ordered row
+    uint32_t sub[2048];     // refine histogram
+    uint32_t list[kBrute];  // b1's values
   } x;
 };
 
-__device__ __forceinline__ uint32_t coarse_count(const uint32_t* c, int b) {
-  uint32_t s = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) s += (c[q * 1024 + (b >> 1)] >> ((b & 1) * 16)) & 0xFFFFu;
-  return s;
-}
-
-// Owner search over nb bins (per thread `per` consecutive bins from the
-// top): returns the bin holding the rank-th item, the items above it and
-// its own count.  `cnt` is read through `get(b)`.
+// Owner search over nb bins from the top (thread t owns nb/kBT consecutive
+// bins, highest first): the bin holding the want-th item from the top, the
+// items above it and its count.  get(b) reads bin b's count.
 template <class Get>
-__device__ __forceinline__ void block_find_bin(Get get, int nb, int rank, int* red,
-                                               uint32_t* bin, int* above, int* count) {
+__device__ __forceinline__ void find_from_top(Get get, int nb, int want, int* red, int* bin,
+                                              int* above, int* count) {
   const int t = threadIdx.x;
   const int per = nb / kBT;
   const int first = nb - 1 - t * per;
   int c = 0;
-  for (int j = 0; j < per; ++j) c += (int)get(first - ((j + t) & (per - 1)));
+  for (int j = 0; j < per; ++j) c += (int)get(first - j);
   int tot;
   const int ab = block_excl_scan<kBT>(c, red, &tot);
-  if (ab < rank && ab + c >= rank) {
+  if (ab < want && ab + c >= want) {
     int acc = ab;
     for (int j = 0; j < per; ++j) {
       const int h = (int)get(first - j);
-      if (acc + h >= rank) {
+      if (acc + h >= want) {
         red[kBT / 64] = first - j;
         red[kBT / 64 + 1] = acc;
         red[kBT / 64 + 2] = h;
@@ -162,7 +152,7 @@ __device__ __forceinline__ void block_find_bin(Get get, int nb, int rank, int* r
     }
   }
   __syncthreads();
-  *bin = (uint32_t)red[kBT / 64];
+  *bin = red[kBT / 64];
   *above = red[kBT / 64 + 1];
   *count = red[kBT / 64 + 2];
   __syncthreads();
@@ -170,14 +160,17 @@ __device__ __forceinline__ void block_find_bin(Get get, int nb, int rank, int* r
 
 __global__ __launch_bounds__(kBT) void topk_block(TopkArgs a) {
   __shared__ BlockSmem sm;
-  __shared__ int red[kBT / 64 + 4];
-  __shared__ uint32_t wred[2][kBT / 64];
+  __shared__ int red[kBT / 64 + 8];
+  __shared__ float fred[2][kBT / 64];
+  __shared__ uint32_t wred[kBT / 64];
   __shared__ int lcount;
-  const int t = threadIdx.x;
-  int r = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  int r = (int)blockIdx.x;
   if (a.row_list) {
     if (r >= *a.row_count) return;
     r = a.row_list[r];
+  } else {
+    r = a.n_rows - 1 - r;  // causal rows grow with the index: longest first
   }
   int64_t off;
   const int64_t n64 =
@@ -196,244 +189,343 @@ __global__ __launch_bounds__(kBT) void topk_block(TopkArgs a) {
     }
     return;
   }
+  const bool select = n > K;
+  // bit i: position p0 + i is visible.  Only the thread holding the row's
+  // end (and threads past it) has invalid positions; it takes the slow
+  // paths, every other thread the branch-free ones.
+  const int nv = n - p0;
+  const uint32_t vm = nv >= kBPer ? 0xFFFFFFFFu : (nv <= 0 ? 0u : (1u << nv) - 1u);
+  const bool full = vm == 0xFFFFFFFFu;
 
-  // A. load + keys + coarse histogram + key range
-  for (int i = t; i < 4096; i += kBT) sm.coarse[i] = 0u;
+  // A. load.  A NaN score is taken as -inf (its order is unspecified; this
+  //    makes every comparison below a total preorder on floats, -0 == +0).
+  for (int i = t; i < kBins; i += kBT) sm.bins[i] = 0u;
   if (t == 0) lcount = 0;
-  uint32_t u[kBPer];
+  auto clean = [](float v) { return v == v ? v : -__builtin_inff(); };
+  float x[kBPer];
   {
-    const uint32_t* rowb = reinterpret_cast<const uint32_t*>(row);
+    const float* rp = row + p0;
     const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+    if (vec && full) {  // 16-byte loads, all in flight at once
 #pragma unroll
-    for (int v = 0; v < kBPer / 4; ++v) {  // every load in flight before the first use
-      const int p = p0 + 4 * v;
-      if (vec && p + 4 <= n) {
-        const uint4 x = *reinterpret_cast<const uint4*>(rowb + p);
-        u[4 * v + 0] = x.x;
-        u[4 * v + 1] = x.y;
-        u[4 * v + 2] = x.z;
-        u[4 * v + 3] = x.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) u[4 * v + e] = p + e < n ? rowb[p + e] : 0u;
+      for (int v = 0; v < kBPer / 4; ++v) {
+        const float4 q = reinterpret_cast<const float4*>(rp)[v];
+        x[4 * v + 0] = q.x;
+        x[4 * v + 1] = q.y;
+        x[4 * v + 2] = q.z;
+        x[4 * v + 3] = q.w;
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kBPer; ++i) x[i] = ((vm >> i) & 1u) ? rp[i] : 0.0f;
     }
   }
-  __syncthreads();
-  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
-  {
-    uint32_t* rep = sm.coarse + (t & 3) * 1024;
+  float vlo = __builtin_inff(), vhi = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < kBPer; ++i) x[i] = clean(x[i]);
+  if (full) {
 #pragma unroll
     for (int i = 0; i < kBPer; ++i) {
-      const bool valid = p0 + i < n;
-      u[i] = valid ? order_key(__uint_as_float(u[i])) : 0u;
-      if (valid) {
-        kmax = u[i] > kmax ? u[i] : kmax;
-        kmin = u[i] < kmin ? u[i] : kmin;
-        const uint32_t b = u[i] >> 21;
-        atomicAdd(&rep[b >> 1], 1u << ((b & 1u) * 16));
+      vlo = __builtin_fminf(vlo, x[i]);
+      vhi = __builtin_fmaxf(vhi, x[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i)
+      if ((vm >> i) & 1u) {
+        vlo = __builtin_fminf(vlo, x[i]);
+        vhi = __builtin_fmaxf(vhi, x[i]);
+      }
+  }
+  {
+    const uint32_t klo = __ockl_wfred_min_u32(order_key(vlo));
+    const uint32_t khi = __ockl_wfred_max_u32(order_key(vhi));
+    if (lane == 0) {
+      fred[0][wid] = key_to_float(klo);
+      fred[1][wid] = key_to_float(khi);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kBT / 64; ++i) {
+    vlo = __builtin_fminf(vlo, fred[0][i]);
+    vhi = __builtin_fmaxf(vhi, fred[1][i]);
+  }
+
+  // B. histogram over kBins bins linear in score value over [vmin, vmax]:
+  //    bin(v) = (v - vmin) * scale rounded down, scale = (kBins - 0.01) /
+  //    (vmax - vmin), so bin(vmax) < kBins after rounding.  bin() is
+  //    monotone, so every item of a higher bin is greater than every item
+  //    of a lower one.  A row without a finite positive span (all equal,
+  //    infinities) puts everything in bin 0 and takes the general paths.
+  //    (readfirstlane takes an int: broadcast the bit patterns.)
+  const float vmin = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vlo)));
+  const float vmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vhi)));
+  const float span = vmax - vmin;
+  const float scale0 = ((float)kBins - 0.01f) / span;
+  const bool flat = !(span > 0.0f) || !(span <= 3.0e38f) || !(scale0 <= 3.0e38f);
+  const float scale = flat ? 0.0f : scale0;
+  // the 32 bins are computed once and kept packed, two per register
+  // (positions past the row's end hold vmin, so every conversion is in range)
+  if (!full) {
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) x[i] = ((vm >> i) & 1u) ? x[i] : vmin;
+  }
+  uint32_t pk[kBPer / 2];
+  if (flat) {
+#pragma unroll
+    for (int j = 0; j < kBPer / 2; ++j) pk[j] = 0u;
+  } else {
+#pragma unroll
+    for (int j = 0; j < kBPer / 2; ++j)
+      pk[j] = (uint32_t)((x[2 * j] - vmin) * scale) |
+              ((uint32_t)((x[2 * j + 1] - vmin) * scale) << 16);
+  }
+  auto bin_of = [&](int i) -> uint32_t { return (pk[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu; };
+  auto bin = [&](float v) -> uint32_t { return flat ? 0u : (uint32_t)((v - vmin) * scale); };
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) atomicAdd(&sm.bins[bin_of(i)], 1u);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i)
+      if ((vm >> i) & 1u) atomicAdd(&sm.bins[bin_of(i)], 1u);
+  }
+  __syncthreads();
+
+  // C. b1 and the packed per-bin (offset << 16 | selected count), from the
+  //    top; thread t owns the kBinsPer bins below kBins - kBinsPer t
+  const int want = select ? K : n;
+  int b1, ab1, in_bin;
+  {
+    const int top = kBins - 1 - kBinsPer * t;  // highest bin of this thread
+    uint32_t c[kBinsPer];
+#pragma unroll
+    for (int v = 0; v < kBinsPer / 4; ++v) {
+      const uint4 q = *reinterpret_cast<const uint4*>(&sm.bins[top - 3 - 4 * v]);
+      c[4 * v + 0] = q.w;
+      c[4 * v + 1] = q.z;
+      c[4 * v + 2] = q.y;
+      c[4 * v + 3] = q.x;
+    }
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < kBinsPer; ++j) sum += (int)c[j];
+    int tot;
+    const int ab = block_excl_scan<kBT>(sum, red, &tot);
+    if (ab < want && ab + sum >= want) {
+      int acc = ab;
+#pragma unroll
+      for (int j = 0; j < kBinsPer; ++j) {
+        if (acc < want && acc + (int)c[j] >= want) {
+          red[kBT / 64] = top - j;
+          red[kBT / 64 + 1] = acc;
+          red[kBT / 64 + 2] = (int)c[j];
+        }
+        acc += (int)c[j];
       }
     }
-  }
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t y = (uint32_t)__shfl_xor((int)kmax, o, 64);
-    const uint32_t z = (uint32_t)__shfl_xor((int)kmin, o, 64);
-    kmax = y > kmax ? y : kmax;
-    kmin = z < kmin ? z : kmin;
-  }
-  if ((t & 63) == 0) {
-    wred[0][t >> 6] = kmax;
-    wred[1][t >> 6] = kmin;
+    __syncthreads();
+    b1 = red[kBT / 64];
+    ab1 = red[kBT / 64 + 1];
+    in_bin = red[kBT / 64 + 2];
+    // selected counts: all of every bin above b1, want - ab1 of b1; output
+    // offsets are the exclusive prefix from the top
+    uint32_t o = (uint32_t)ab, crowd = 0u;
+#pragma unroll
+    for (int j = 0; j < kBinsPer; ++j) {
+      const int b = top - j;
+      const uint32_t sel = b > b1 ? c[j] : (b == b1 ? (uint32_t)(want - ab1) : 0u);
+      const uint32_t cj = c[j];
+      c[j] = (o << 16) | sel;
+      crowd = sel > crowd ? sel : crowd;
+      o += cj;
+    }
+#pragma unroll
+    for (int v = 0; v < kBinsPer / 4; ++v)
+      *reinterpret_cast<uint4*>(&sm.bins[top - 3 - 4 * v]) =
+          make_uint4(c[4 * v + 3], c[4 * v + 2], c[4 * v + 1], c[4 * v + 0]);
+    crowd = __ockl_wfred_max_u32(crowd);
+    if (lane == 0) wred[wid] = crowd;
   }
   __syncthreads();
-  for (int i = 0; i < kBT / 64; ++i) {
-    kmax = wred[0][i] > kmax ? wred[0][i] : kmax;
-    kmin = wred[1][i] < kmin ? wred[1][i] : kmin;
-  }
-  const bool select = n > K;
-
-  // B. the coarse bin of the K-th item (or, selecting everything, of the
-  //    smallest key), then packed per-bin (offset << 16 | selected count)
-  uint32_t b1;
-  int ab1, in_bin;
-  {
-    const int want = select ? K : n;
-    block_find_bin([&](int b) { return coarse_count(sm.coarse, b); }, 2048, want, red, &b1, &ab1,
-                   &in_bin);
-  }
-  const int rank = (select ? K : n) - ab1;  // items wanted from bin b1
-  {
-    // thread t owns bins 2047 - 8 t .. 2040 - 8 t
-    uint32_t c8[8];
-    int s = 0;
+  uint32_t crowd = 0u;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int b = 2047 - 8 * t - j;
-      c8[j] = (uint32_t)b >= b1 ? coarse_count(sm.coarse, b) : 0u;
-      if ((uint32_t)b == b1) c8[j] = (uint32_t)rank;
-      s += (int)c8[j];
-    }
-    int tot;
-    int o = block_excl_scan<kBT>(s, red, &tot);  // its trailing sync orders the reads
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int b = 2047 - 8 * t - j;
-      sm.coarse[b] = ((uint32_t)o << 16) | c8[j];
-      o += (int)c8[j];
-    }
-  }
-  __syncthreads();
+  for (int i = 0; i < kBT / 64; ++i) crowd = wred[i] > crowd ? wred[i] : crowd;
 
-  // C. exact threshold key inside bin b1
-  uint32_t thr = 0u;
+  // D. the exact threshold value T inside b1
+  float thr = 0.0f;
   int n_gt = 0, n_eq = 0;
   if (select) {
-    uint32_t d2, d3;
-    int ab2, ab3, c2;
-    for (int i = t; i < 2048; i += kBT) sm.x.r.rh[i] = 0u;
-    if (in_bin <= 2048) {
+    const int need = K - ab1;  // rank of T among b1's items, >= 1
+    uint32_t inb = 0u;         // which of this thread's items lie in b1
 #pragma unroll
-      for (int i = 0; i < kBPer; ++i)
-        if (p0 + i < n && (u[i] >> 21) == b1) sm.x.r.list[atomicAdd(&lcount, 1)] = u[i];
-      __syncthreads();
-      for (int i = t; i < in_bin; i += kBT) {
-        const uint32_t v = sm.x.r.list[i];
-        atomicAdd(&sm.x.r.rh[(v >> 10) & 2047u], 1u);
+    for (int i = 0; i < kBPer; ++i) inb |= ((int)bin_of(i) == b1) ? (1u << i) : 0u;
+    inb &= vm;
+    if (in_bin <= kBrute) {
+      // b1 holds few items: each position is a uniform skip unless some
+      // lane of the wave has one there (the mask is re-derived per position
+      // so the compiler does not hold 32 of them)
+#pragma unroll
+      for (int i = 0; i < kBPer; ++i) {
+        asm volatile("" : "+v"(inb));
+        if ((inb >> i) & 1u) sm.x.list[atomicAdd(&lcount, 1)] = __float_as_uint(x[i]);
       }
-    } else {
       __syncthreads();
-#pragma unroll
-      for (int i = 0; i < kBPer; ++i)
-        if (p0 + i < n && (u[i] >> 21) == b1) atomicAdd(&sm.x.r.rh[(u[i] >> 10) & 2047u], 1u);
-    }
-    __syncthreads();
-    block_find_bin([&](int b) { return sm.x.r.rh[b]; }, 2048, rank, red, &d2, &ab2, &c2);
-    const uint32_t pre2 = (b1 << 21) | (d2 << 10);
-    for (int i = t; i < 1024; i += kBT) sm.x.r.rh[i] = 0u;
-    __syncthreads();
-    if (in_bin <= 2048) {
-      for (int i = t; i < in_bin; i += kBT) {
-        const uint32_t v = sm.x.r.list[i];
-        if ((v >> 10) == (pre2 >> 10)) atomicAdd(&sm.x.r.rh[v & 1023u], 1u);
+      if (t < in_bin) {
+        const float me = __uint_as_float(sm.x.list[t]);
+        int g = 0, e = 0;
+        for (int j = 0; j < in_bin; ++j) {
+          const float v = __uint_as_float(sm.x.list[j]);
+          g += v > me ? 1 : 0;
+          e += v == me ? 1 : 0;
+        }
+        if (g < need && need <= g + e) {  // every holder of T writes the same values
+          red[kBT / 64 + 3] = (int)__float_as_uint(me);
+          red[kBT / 64 + 4] = g;
+          red[kBT / 64 + 5] = e;
+        }
       }
+      __syncthreads();
+      thr = __uint_as_float((uint32_t)red[kBT / 64 + 3]);
+      n_gt = ab1 + red[kBT / 64 + 4];
+      n_eq = red[kBT / 64 + 5];
     } else {
-#pragma unroll
-      for (int i = 0; i < kBPer; ++i)
-        if (p0 + i < n && (u[i] >> 10) == (pre2 >> 10)) atomicAdd(&sm.x.r.rh[u[i] & 1023u], 1u);
+      // radix select among b1's items on the key digits 11/11/10; this rare
+      // path re-reads b1's scores (from cache) rather than tying up the
+      // register-resident row
+      uint32_t prefix = 0u, pmask = 0u;
+      int rank = need, above = ab1, count = in_bin;
+#pragma unroll 1
+      for (int level = 0; level < 3; ++level) {
+        const int sh = level == 0 ? 21 : (level == 1 ? 10 : 0);
+        const uint32_t dmask = level == 2 ? 1023u : 2047u;
+        for (int i = t; i < 2048; i += kBT) sm.x.sub[i] = 0u;
+        __syncthreads();
+        asm volatile("" : "+v"(inb));
+        for (uint32_t mb = inb; mb != 0u; mb &= mb - 1u) {
+          const uint32_t k = order_key(clean(row[p0 + __builtin_ctz(mb)]));
+          if ((k & pmask) == prefix) atomicAdd(&sm.x.sub[(k >> sh) & dmask], 1u);
+        }
+        __syncthreads();
+        int dig, ab;
+        find_from_top([&](int b) { return sm.x.sub[b]; }, 2048, rank, red, &dig, &ab, &count);
+        rank -= ab;
+        above += ab;
+        prefix |= (uint32_t)dig << sh;
+        pmask |= dmask << sh;
+      }
+      thr = key_to_float(prefix);
+      n_gt = above;
+      n_eq = count;
     }
-    __syncthreads();
-    block_find_bin([&](int b) { return sm.x.r.rh[b]; }, 1024, rank - ab2, red, &d3, &ab3, &n_eq);
-    thr = pre2 | d3;
-    n_gt = ab1 + ab2 + ab3;
   }
 
-  // D. index-ordered compaction into the dense list
+  // E. scatter the selected items grouped by bin (cursor = packed high half)
   const int need_eq = select ? K - n_gt : 0;
   {
-    int c_gt = 0, c_eq = 0;
+    // selection mask: everything (no selection), or > T plus the first
+    // `take` positions == T of this thread in index order
+    uint32_t selm = vm;
+    if (select) {
+      uint32_t gtm = 0u, eqm = 0u;
 #pragma unroll
-    for (int i = 0; i < kBPer; ++i) {
-      const bool valid = p0 + i < n;
-      c_gt += (valid && u[i] > thr) ? 1 : 0;
-      c_eq += (valid && select && u[i] == thr) ? 1 : 0;
+      for (int i = 0; i < kBPer; ++i) {
+        gtm |= x[i] > thr ? (1u << i) : 0u;
+        eqm |= x[i] == thr ? (1u << i) : 0u;
+      }
+      gtm &= vm;
+      eqm &= vm;
+      const int c_eq = __builtin_popcount(eqm);
+      int eq_before = 0, tot;
+      if (need_eq < n_eq) eq_before = block_excl_scan<kBT>(c_eq, red, &tot);  // uniform branch
+      int take = need_eq - eq_before;
+      take = take < 0 ? 0 : (take > c_eq ? c_eq : take);
+      for (int k = c_eq - take; k > 0; --k) eqm &= ~(1u << (31 - __builtin_clz(eqm)));  // drop the highest
+      selm = gtm | eqm;
     }
-    int tot;
-    int eq_before = 0;
-    if (need_eq < n_eq) eq_before = block_excl_scan<kBT>(c_eq, red, &tot);  // uniform branch
-    int take = need_eq - eq_before;
-    take = take < 0 ? 0 : (take > c_eq ? c_eq : take);
-    int w = block_excl_scan<kBT>(c_gt + take, red, &tot);
-    int taken = 0;
+    // eight returning cursor atomics in flight, then their eight stores
 #pragma unroll
-    for (int i = 0; i < kBPer; ++i) {
-      const bool valid = p0 + i < n;
-      const bool sel =
-          valid && (u[i] > thr || (select && u[i] == thr && taken++ < take));
-      if (sel) sm.x.dense[w++] = ((uint64_t)u[i] << 32) | (uint32_t)(~(uint32_t)(p0 + i));
+    for (int c = 0; c < kBPer / 8; ++c) {
+      uint32_t pos[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = 8 * c + k;
+        pos[k] = 0u;
+        if ((selm >> i) & 1u) pos[k] = atomicAdd(&sm.bins[bin_of(i)], 0x10000u) >> 16;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = 8 * c + k;
+        if ((selm >> i) & 1u) {
+          // orderable key (-0 folded onto +0) into a fresh register: the
+          // 64-bit store takes an aligned pair, and a copy keeps the
+          // compiler from pinning all 32 items to pairs
+          uint32_t kc;
+          asm volatile("v_mov_b32 %0, %1" : "=v"(kc) : "v"(order_key(x[i])));
+          sm.x.comp[pos[k]] = ((uint64_t)kc << 32) | (uint32_t)(~(uint32_t)(p0 + i));
+        }
+      }
     }
   }
   __syncthreads();
 
-  // E. bucket rank
-  uint64_t it[kBItems];
+  if (crowd <= (uint32_t)kCrowd) {
+    // rank inside the bin: after the scatter a bin's packed word is
+    // ((offset + count) << 16 | count).  The bin is scanned four entries per
+    // step with no branch in the step: four independent LDS reads (index
+    // clamped inside the list), then masked compares.
+    uint64_t it[kBItems];
+    uint32_t dst[kBItems];
 #pragma unroll
-  for (int i = 0; i < kBItems; ++i) {
-    const int q = kBItems * t + i;
-    it[i] = q < cnt ? sm.x.dense[q] : 0ull;
+    for (int m = 0; m < kBItems; ++m) {
+      const int q = kBItems * t + m;
+      it[m] = 0ull;
+      dst[m] = 0u;
+      if (q < cnt) {
+        it[m] = sm.x.comp[q];
+        const uint32_t w = sm.bins[bin(key_to_float((uint32_t)(it[m] >> 32)))];
+        const uint32_t len = w & 0xFFFFu, s0 = (w >> 16) - len;
+        uint32_t rk = 0u;
+        for (uint32_t j = 0; j < len; j += 4) {
+          uint64_t v[4];
+#pragma unroll
+          for (uint32_t k = 0; k < 4; ++k) {
+            const uint32_t x2 = s0 + j + k;
+            v[k] = sm.x.comp[x2 < (uint32_t)kBK ? x2 : (uint32_t)kBK - 1u];
+          }
+#pragma unroll
+          for (uint32_t k = 0; k < 4; ++k)
+            rk += (uint32_t)(j + k < len) & (uint32_t)(v[k] > it[m]);
+        }
+        dst[m] = s0 + rk;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < kBItems; ++m)
+      if (kBItems * t + m < cnt) sm.x.comp[dst[m]] = it[m];
+    __syncthreads();
+  } else {
+    const int P = next_pow2(cnt);
+    for (int q = cnt + t; q < P; q += kBT) sm.x.comp[q] = 0ull;
+    __syncthreads();
+    bitonic_sort_desc<kBT>(sm.x.comp, P);
   }
-  auto emit = [&](uint32_t dst, uint64_t c) {
-    const uint32_t p = ~(uint32_t)c;
-    oi[dst] = a.id_map ? a.id_map[p] : (int32_t)p;
-    if (os) os[dst] = key_to_float((uint32_t)(c >> 32));
-  };
-  const uint32_t kmin_sel = select ? thr : kmin;
-  if (cnt > 0 && kmin_sel == kmax) {
-    // one distinct key: index order, already the dense order
-#pragma unroll
-    for (int i = 0; i < kBItems; ++i)
-      if (kBItems * t + i < cnt) emit((uint32_t)(kBItems * t + i), it[i]);
-  } else if (cnt > 0) {
-    uint32_t* bcnt = sm.coarse + 2048;  // bucket b at (b & 7) * 256 + (b >> 3)
-    auto bsw = [](uint32_t b) { return ((b & 7u) << 8) | (b >> 3); };
-    const uint32_t lo_thr = kmin_sel & 0x1FFFFFu;
-    uint32_t bk[kBItems];
-#pragma unroll
-    for (int i = 0; i < kBItems; ++i) {
-      bk[i] = 0;
-      if (kBItems * t + i < cnt) {
-        const uint32_t key = (uint32_t)(it[i] >> 32);
-        const uint32_t cb = key >> 21, pk = sm.coarse[cb];
-        const uint32_t o = pk >> 16, c = pk & 0xFFFFu;
-        const uint32_t lo = cb == b1 ? lo_thr : 0u;
-        int sub = (int)((float)((key & 0x1FFFFFu) - lo) * ((float)c / (float)(0x200000u - lo)));
-        sub = sub < (int)c - 1 ? sub : (int)c - 1;
-        bk[i] = o + (c - 1 - (uint32_t)sub);  // highest keys first
-      }
+
+  // coalesced output of the ordered row, then the padding.  Positions are
+  // < n by construction; the clamp only keeps an id_map lookup in bounds.
+  for (int q = t; q < K; q += kBT) {
+    if (q < cnt) {
+      const uint64_t c = sm.x.comp[q];
+      uint32_t p = ~(uint32_t)c;
+      p = p < (uint32_t)n ? p : 0u;
+      oi[q] = a.id_map ? a.id_map[p] : (int32_t)p;
+      if (os) os[q] = key_to_float((uint32_t)(c >> 32));
+    } else {
+      oi[q] = -1;
+      if (os) os[q] = -__builtin_inff();
     }
-    for (int i = t; i < 2048; i += kBT) bcnt[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kBItems; ++i)
-      if (kBItems * t + i < cnt) atomicAdd(&bcnt[bsw(bk[i])], 1u);
-    __syncthreads();
-    {
-      uint32_t c8[8];
-      int s = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        c8[j] = bcnt[(j << 8) | t];
-        s += (int)c8[j];
-      }
-      int tot;
-      uint32_t o = (uint32_t)block_excl_scan<kBT>(s, red, &tot);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        bcnt[(j << 8) | t] = o << 16;  // offset, cursor 0
-        o += c8[j];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kBItems; ++i)
-      if (kBItems * t + i < cnt) {
-        const uint32_t w = atomicAdd(&bcnt[bsw(bk[i])], 1u);
-        sm.x.dense[(w >> 16) + (w & 0xFFFFu)] = it[i];
-      }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kBItems; ++i) {
-      if (kBItems * t + i < cnt) {
-        const uint32_t w = bcnt[bsw(bk[i])];
-        const uint32_t s0 = w >> 16, s1 = s0 + (w & 0xFFFFu);
-        uint32_t rk = 0;
-        for (uint32_t x = s0; x < s1; ++x) rk += sm.x.dense[x] > it[i] ? 1u : 0u;
-        emit(s0 + rk, it[i]);
-      }
-    }
-  }
-  for (int q = cnt + t; q < K; q += kBT) {
-    oi[q] = -1;
-    if (os) os[q] = -__builtin_inff();
   }
 }
 

@@ -25,6 +25,15 @@ def _rows(kind, rng, n_rows, L):
     if kind == "wide":
         return (rng.standard_normal((n_rows, L)) *
                 np.exp(rng.uniform(-20, 20, (n_rows, L)))).astype(np.float32)
+    if kind == "nan_inf":  # non-finite scores mixed into a normal row
+        x = rng.standard_normal((n_rows, L)).astype(np.float32)
+        m = rng.random((n_rows, L))
+        x[m < 0.01] = np.nan
+        x[(m >= 0.01) & (m < 0.015)] = np.inf
+        x[(m >= 0.015) & (m < 0.02)] = -np.inf
+        return x
+    if kind == "bits":  # arbitrary 32-bit patterns: NaNs, infinities, subnormals
+        return rng.integers(0, 2**32, (n_rows, L), dtype=np.uint64).astype(np.uint32).view(np.float32)
     raise ValueError(kind)
 
 
@@ -37,12 +46,15 @@ def _check(orc, scores, vis, K):
     gi, gs = gi.cpu().numpy(), gs.cpu().numpy()
     for r in range(scores.shape[0]):
         v = int(min(max(vis[r], 0), scores.shape[1]))
-        oi, os_, _ = orc.topk(scores[r, :v].astype(np.float64), K)
+        # a NaN score ranks as -inf (its order is otherwise unspecified)
+        row = np.where(np.isnan(scores[r, :v]), -np.inf, scores[r, :v]).astype(np.float64)
+        oi, os_, _ = orc.topk(row, K)
         np.testing.assert_array_equal(gi[r], oi, err_msg=f"row {r} n={v} K={K}")
         np.testing.assert_array_equal(gs[r].astype(np.float64), os_, err_msg=f"row {r}")
 
 
-@pytest.mark.parametrize("kind", ["normal", "equal", "few_values", "narrow", "signed_zero", "wide"])
+@pytest.mark.parametrize("kind", ["normal", "equal", "few_values", "narrow", "signed_zero", "wide",
+                                  "nan_inf", "bits"])
 @pytest.mark.parametrize("L,K", [(8192, 2048), (5000, 2048), (3000, 100), (8192, 1), (700, 513)])
 def test_short_rows(orc, kind, L, K):
     rng = np.random.default_rng(L + K)
