@@ -140,9 +140,12 @@ def bench_indexer(args, cfg, workload):
         si.idx_score(d["q"], d["k"], d["w"], d["vis_len"], k_scale=d["k_scale"],
                      k_row_offset=d["k_row_offset"], max_vis=mv, out_scores=scores)
 
+    topk_ws = torch.empty(max(si.lib().rows_topk_workspace(n_q, mv, K), 1), dtype=torch.uint8,
+                          device=dev)
+
     def topk():
         si.rows_topk(scores, d["vis_len"], K, k_row_offset=d["k_row_offset"], n_k=cfg["n_k"],
-                     max_vis=mv, out_idx=out_idx, want_scores=False)
+                     max_vis=mv, out_idx=out_idx, want_scores=False, workspace=topk_ws)
 
     def witness():
         si.kvwitness_merge(out_idx, d["vis_len"], wit["S"], wit["keep"], wit["max_rep"])

@@ -90,6 +90,9 @@ typedef enum { SI_F32 = 0, SI_BF16 = 1, SI_FP8_E4M3FN = 2 } si_dtype;
  *  out_idx [n_q, K] i32: the top-K of row r (order above), then -1 padding.
  *  out_score [n_q, K] f32 or NULL: their scores, then -inf padding.
  *  q, k must be 16-byte aligned; float outputs 4-byte aligned.
+ *  workspace  idx_score_topk_workspace(...) bytes, 256-byte aligned: the
+ *          score rows and, for max_vis > 8192, the chunked top-K's
+ *          candidate lists.
  * Errors: INVALID_ARGUMENT (null pointer, size <= 0 where one is required,
  * D or H beyond the supported range, misalignment), UNSUPPORTED_DTYPE,
  * WORKSPACE_TOO_SMALL.
@@ -111,7 +114,11 @@ size_t idx_score_topk_workspace(int32_t n_q, int32_t H, int32_t D, int64_t max_v
  *   entries j >= vis_r are not written.
  * rows_topk: top-K of each row's first vis_r scores (vis_r clamped as in
  *   idx_score_topk from vis_len / k_row_offset / n_k / max_vis), written as
- *   idx_score_topk writes them.  scores rows at r * score_stride. */
+ *   idx_score_topk writes them.  scores rows at r * score_stride.  Rows
+ *   longer than 8192 scores (with topk <= 2048) are selected in chunks whose
+ *   candidate lists live in the caller's workspace of
+ *   rows_topk_workspace(n_rows, max_vis, topk) bytes (0 when not needed;
+ *   256-byte aligned); a smaller workspace -> WORKSPACE_TOO_SMALL. */
 si_status idx_score(const void* q, si_dtype q_dtype, const void* k, si_dtype k_dtype,
                     const float* k_scale, const float* w, int64_t w_row_stride,
                     const int64_t* k_row_offset, const int32_t* vis_len, int32_t n_q, int32_t H,
@@ -119,7 +126,9 @@ si_status idx_score(const void* q, si_dtype q_dtype, const void* k, si_dtype k_d
                     int64_t score_stride, hipStream_t stream);
 si_status rows_topk(const float* scores, int64_t score_stride, const int32_t* vis_len,
                     const int64_t* k_row_offset, int64_t n_k, int64_t max_vis, int32_t n_rows,
-                    int32_t topk, int32_t* out_idx, float* out_score, hipStream_t stream);
+                    int32_t topk, int32_t* out_idx, float* out_score, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+size_t rows_topk_workspace(int32_t n_rows, int64_t max_vis, int32_t topk);
 
 /* ------------------------------------------------------------------------ *
  * dosa_prune_topk

@@ -46,7 +46,8 @@ SIGNATURES = {
     "idx_score_topk_workspace": (sz, [i32, i32, i32, i64, i32]),
     "idx_score": (i32, [vp, i32, vp, i32, vp, vp, i64, vp, vp, i32, i32, i32, i64, i64, vp, i64,
                         vp]),
-    "rows_topk": (i32, [vp, i64, vp, vp, i64, i64, i32, i32, vp, vp, vp]),
+    "rows_topk": (i32, [vp, i64, vp, vp, i64, i64, i32, i32, vp, vp, vp, sz, vp]),
+    "rows_topk_workspace": (sz, [i32, i64, i32]),
     "dosa_prune_topk": (i32, [vp, vp, i32, vp, i64, vp, i32, i32, i32, i64, i32, vp, vp, vp, vp,
                               vp, sz, vp]),
     "dosa_prune_topk_workspace": (sz, [i32, i32, i32, i64, i32, vp]),
@@ -114,6 +115,8 @@ def _dtype_code(t, name):
 
 
 def _workspace(nbytes, dev, given):
+    """The caller's workspace, or a fresh one (the caching allocator returns
+    blocks aligned far beyond the 256 bytes the library asks for)."""
     if nbytes == 0:
         return given, 0
     if given is not None:
@@ -178,8 +181,9 @@ def idx_score(q, k, w, vis_len, *, k_scale=None, k_row_offset=None, max_vis=None
 
 
 def rows_topk(scores, vis_len, topk, *, k_row_offset=None, n_k=None, max_vis=None,
-              out_idx=None, out_score=None, want_scores=True):
-    """Top-K of each score row's first vis_r entries; returns (idx, scores|None)."""
+              out_idx=None, out_score=None, want_scores=True, workspace=None):
+    """Top-K of each score row's first vis_r entries; returns (idx, scores|None).
+    Rows longer than 8192 need a workspace (allocated here when not given)."""
     _dev_tensor(scores, "scores", torch.float32)
     _dev_tensor(vis_len, "vis_len", torch.int32)
     dev = scores.device
@@ -192,8 +196,11 @@ def rows_topk(scores, vis_len, topk, *, k_row_offset=None, n_k=None, max_vis=Non
         out_idx = torch.empty((n_rows, topk), dtype=torch.int32, device=dev)
     if out_score is None and want_scores:
         out_score = torch.empty((n_rows, topk), dtype=torch.float32, device=dev)
+    need = lib().rows_topk_workspace(n_rows, max_vis, topk)
+    ws, ws_bytes = _workspace(need, dev, workspace)
     st = lib().rows_topk(_ptr(scores), stride, _ptr(vis_len), _ptr(k_row_offset), n_k, max_vis,
-                         n_rows, topk, _ptr(out_idx), _ptr(out_score), _stream(dev))
+                         n_rows, topk, _ptr(out_idx), _ptr(out_score), _ptr(ws), ws_bytes,
+                         _stream(dev))
     _check(st, "rows_topk")
     return out_idx, out_score
 

@@ -43,11 +43,18 @@ const char* si_status_string(si_status s) {
   return "unknown status";
 }
 
+size_t rows_topk_workspace(int32_t n_rows, int64_t max_vis, int32_t topk) {
+  if (n_rows <= 0 || max_vis <= 0 || topk < 1) return 0;
+  return topk_workspace_bytes(n_rows, max_vis, topk);
+}
+
+// idx_score_topk's workspace: the score rows, then (256-byte aligned) the
+// candidate lists of the chunked top-K for long rows
 size_t idx_score_topk_workspace(int32_t n_q, int32_t H, int32_t D, int64_t max_vis, int32_t topk) {
   (void)H;
   (void)D;
-  (void)topk;
-  return score_ws_bytes(n_q, max_vis);
+  const size_t s = (score_ws_bytes(n_q, max_vis) + 255) & ~(size_t)255;
+  return s + rows_topk_workspace(n_q, max_vis, topk);
 }
 
 // Checks shared by idx_score and idx_score_topk; fills `sa` (scores unset).
@@ -92,7 +99,8 @@ si_status idx_score(const void* q, si_dtype q_dtype, const void* k, si_dtype k_d
 
 si_status rows_topk(const float* scores, int64_t score_stride, const int32_t* vis_len,
                     const int64_t* k_row_offset, int64_t n_k, int64_t max_vis, int32_t n_rows,
-                    int32_t topk, int32_t* out_idx, float* out_score, hipStream_t stream) {
+                    int32_t topk, int32_t* out_idx, float* out_score, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
   if (n_rows < 0 || n_k < 0 || max_vis < 0 || max_vis > INT32_MAX || topk < 1 ||
       topk > kMaxTopk || score_stride < max_vis)
     return SI_ERR_INVALID_ARGUMENT;
@@ -100,10 +108,14 @@ si_status rows_topk(const float* scores, int64_t score_stride, const int32_t* vi
   if ((max_vis > 0 && !scores) || !vis_len || !out_idx || !aligned4(out_idx) ||
       (out_score && !aligned4(out_score)) || (scores && !aligned4(scores)))
     return SI_ERR_INVALID_ARGUMENT;
+  const size_t need = rows_topk_workspace(n_rows, max_vis, topk);
+  if (need && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255)))
+    return SI_ERR_WORKSPACE_TOO_SMALL;
   TopkArgs ta;
   ta.scores = scores; ta.stride = score_stride; ta.vis_len = vis_len;
   ta.k_row_offset = k_row_offset; ta.n_k = n_k; ta.max_vis = max_vis; ta.n_rows = n_rows;
   ta.K = topk; ta.out_idx = out_idx; ta.out_score = out_score; ta.id_map = nullptr;
+  ta.workspace = workspace; ta.workspace_bytes = workspace_bytes;
   return launch_topk(ta, stream) == hipSuccess ? SI_OK : SI_ERR_DEVICE;
 }
 
@@ -121,10 +133,12 @@ si_status idx_score_topk(const void* q, si_dtype q_dtype, const void* k, si_dtyp
   if (n_q == 0) return SI_OK;
   if (!out_idx || !aligned4(out_idx) || (out_score && !aligned4(out_score)))
     return SI_ERR_INVALID_ARGUMENT;
-  const size_t need = score_ws_bytes(n_q, max_vis);
-  if (need && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+  const size_t need = idx_score_topk_workspace(n_q, H, D, max_vis, topk);
+  if (need && (!workspace || workspace_bytes < need ||
+               (reinterpret_cast<uintptr_t>(workspace) & 255)))
     return SI_ERR_WORKSPACE_TOO_SMALL;
   sa.scores = reinterpret_cast<float*>(workspace);
+  const size_t cand_off = (score_ws_bytes(n_q, max_vis) + 255) & ~(size_t)255;
 
   hipError_t e = launch_score(sa, stream);
   if (e != hipSuccess) return SI_ERR_DEVICE;
@@ -132,6 +146,8 @@ si_status idx_score_topk(const void* q, si_dtype q_dtype, const void* k, si_dtyp
   ta.scores = sa.scores; ta.stride = max_vis; ta.vis_len = vis_len; ta.k_row_offset = k_row_offset;
   ta.n_k = n_k; ta.max_vis = max_vis; ta.n_rows = n_q; ta.K = topk; ta.out_idx = out_idx;
   ta.out_score = out_score; ta.id_map = nullptr;
+  ta.workspace = static_cast<unsigned char*>(workspace) + cand_off;
+  ta.workspace_bytes = workspace_bytes - cand_off;
   e = launch_topk(ta, stream);
   return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
 }

@@ -199,8 +199,18 @@ struct TopkArgs {
   const int32_t* id_map = nullptr;     // optional increasing map position -> id
   const int32_t* row_list = nullptr;   // optional: only rows row_list[0 .. *row_count)
   const int32_t* row_count = nullptr;
+  int64_t id_map_stride = 0;           // row r maps through id_map + r * id_map_stride
+  int32_t chunk = 0;                   // > 0: block y takes positions [y chunk, (y+1) chunk)
+  int64_t out_stride = 0;              // output row stride (0: K); chunk y writes at y K
+  void* workspace = nullptr;           // candidate lists for rows longer than one block
+  size_t workspace_bytes = 0;
 };
+// Top-K of each row.  Rows of at most 8192 scores with K <= 2048 take one
+// workgroup each; longer rows are cut into 8192-score chunks whose ordered
+// top-K lists are selected from again (needs topk_workspace_bytes of
+// workspace; without it, or for K > 2048, a single-workgroup radix select).
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+size_t topk_workspace_bytes(int64_t n_rows, int64_t max_vis, int K);
 constexpr int kMaxTopk = 4096;
 hipError_t launch_score_rows_listed(const ScoreArgs& a, const int32_t* row_list,
                                     const int32_t* row_count, hipStream_t st);

@@ -173,14 +173,26 @@ __global__ __launch_bounds__(kBT) void topk_block(TopkArgs a) {
     r = a.n_rows - 1 - r;  // causal rows grow with the index: longest first
   }
   int64_t off;
-  const int64_t n64 =
+  int64_t n64 =
       a.vis_len ? visible_len(a.vis_len, a.k_row_offset, r, a.n_k, a.max_vis, &off) : a.max_vis;
-  const int n = (int)(n64 < kBN ? n64 : kBN);
   const int K = a.K;
+  // chunk mode: this block takes positions [start, start + chunk) of the row
+  // and writes its ordered top-K at y K of the output row; an empty chunk
+  // writes nothing (the next level never reads it)
+  const int64_t start = a.chunk > 0 ? (int64_t)blockIdx.y * a.chunk : 0;
+  if (a.chunk > 0) {
+    n64 -= start;
+    if (n64 <= 0) return;
+    n64 = n64 < a.chunk ? n64 : a.chunk;
+  }
+  const int n = (int)(n64 < kBN ? n64 : kBN);
   const int cnt = n < K ? n : K;
-  const float* row = a.scores + (int64_t)r * a.stride;
-  int32_t* oi = a.out_idx + (int64_t)r * K;
-  float* os = a.out_score ? a.out_score + (int64_t)r * K : nullptr;
+  const float* row = a.scores + (int64_t)r * a.stride + start;
+  const int64_t ostride = a.out_stride > 0 ? a.out_stride : K;
+  const int64_t obase = (int64_t)r * ostride + (a.chunk > 0 ? (int64_t)blockIdx.y * K : 0);
+  int32_t* oi = a.out_idx + obase;
+  float* os = a.out_score ? a.out_score + obase : nullptr;
+  const int32_t* idmap = a.id_map ? a.id_map + (int64_t)r * a.id_map_stride + start : nullptr;
   const int p0 = kBPer * t;
   if (n <= 0) {
     for (int q = t; q < K; q += kBT) {
@@ -520,7 +532,7 @@ __global__ __launch_bounds__(kBT) void topk_block(TopkArgs a) {
       const uint64_t c = sm.x.comp[q];
       uint32_t p = ~(uint32_t)c;
       p = p < (uint32_t)n ? p : 0u;
-      oi[q] = a.id_map ? a.id_map[p] : (int32_t)p;
+      oi[q] = idmap ? idmap[p] : (int32_t)(start + p);
       if (os) os[q] = key_to_float((uint32_t)(c >> 32));
     } else {
       oi[q] = -1;
@@ -529,13 +541,88 @@ __global__ __launch_bounds__(kBT) void topk_block(TopkArgs a) {
   }
 }
 
+// Candidate count of each row after a chunk pass: every full chunk keeps K,
+// the last one min(K, its length).  Rows follow the same row list.
+__global__ void topk_next_len(TopkArgs a, int32_t* out_len) {
+  int r = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (r >= a.n_rows) return;
+  if (a.row_list) {
+    if (r >= *a.row_count) return;
+    r = a.row_list[r];
+  }
+  int64_t off;
+  const int64_t n =
+      a.vis_len ? visible_len(a.vis_len, a.k_row_offset, r, a.n_k, a.max_vis, &off) : a.max_vis;
+  int64_t c = 0;
+  if (n > 0) {
+    const int64_t full = (n - 1) / kBN;  // chunks before the last one
+    const int64_t last = n - full * kBN;
+    c = full * a.K + (last < a.K ? last : a.K);
+  }
+  out_len[r] = (int32_t)c;
+}
+
+// Bytes of one chunk level (candidate ids + scores + per-row counts), and
+// the number of chunks per row of a level with rows of at most len scores.
+static int64_t chunks_of(int64_t len) { return (len + kBN - 1) / kBN; }
+static size_t level_bytes(int64_t n_rows, int64_t len, int K) {
+  const size_t cand = (size_t)n_rows * (size_t)chunks_of(len) * (size_t)K;
+  return ((cand * 8 + (size_t)n_rows * 4) + 255) & ~(size_t)255;
+}
+
+size_t topk_workspace_bytes(int64_t n_rows, int64_t max_vis, int K) {
+  if (K > kBK || max_vis <= kBN || n_rows <= 0) return 0;
+  size_t total = 0;
+  for (int64_t len = max_vis; len > kBN; len = chunks_of(len) * K) total += level_bytes(n_rows, len, K);
+  return total;
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.n_rows == 0) return hipSuccess;
   const dim3 grid((unsigned)a.n_rows);
-  if (a.K <= kBK && a.max_vis <= kBN)
+  if (a.K <= kBK && a.max_vis <= kBN) {
     hipLaunchKernelGGL(topk_block, grid, dim3(kBT), 0, st, a);
-  else
+    return hipGetLastError();
+  }
+  const size_t need = topk_workspace_bytes(a.n_rows, a.max_vis, a.K);
+  if (a.K > kBK || a.workspace == nullptr || a.workspace_bytes < need) {
     hipLaunchKernelGGL(topk_rows, grid, dim3(kTopkThreads), 0, st, a);
+    return hipGetLastError();
+  }
+  // chunk passes until a row's candidates fit one block, then the last pass
+  TopkArgs cur = a;
+  cur.chunk = 0;
+  cur.out_stride = 0;
+  unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+  int64_t len = a.max_vis;
+  while (len > kBN) {
+    const int64_t nch = chunks_of(len);
+    const int64_t cstride = nch * a.K;
+    int32_t* cidx = reinterpret_cast<int32_t*>(ws);
+    float* csc = reinterpret_cast<float*>(ws + (size_t)a.n_rows * cstride * 4);
+    int32_t* clen = reinterpret_cast<int32_t*>(ws + (size_t)a.n_rows * cstride * 8);
+    TopkArgs L = cur;
+    L.chunk = kBN;
+    L.out_idx = cidx;
+    L.out_score = csc;
+    L.out_stride = cstride;
+    hipLaunchKernelGGL(topk_block, dim3((unsigned)a.n_rows, (unsigned)nch), dim3(kBT), 0, st, L);
+    hipLaunchKernelGGL(topk_next_len, dim3((unsigned)((a.n_rows + 255) / 256)), dim3(256), 0, st,
+                       cur, clen);
+    cur.scores = csc;
+    cur.stride = cstride;
+    cur.vis_len = clen;
+    cur.k_row_offset = nullptr;
+    cur.n_k = cstride;
+    cur.max_vis = cstride;
+    cur.id_map = cidx;
+    cur.id_map_stride = cstride;
+    ws += level_bytes(a.n_rows, len, a.K);
+    len = cstride;
+  }
+  cur.out_idx = a.out_idx;
+  cur.out_score = a.out_score;
+  hipLaunchKernelGGL(topk_block, grid, dim3(kBT), 0, st, cur);
   return hipGetLastError();
 }
 
