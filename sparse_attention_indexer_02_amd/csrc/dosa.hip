@@ -53,7 +53,8 @@ struct DosaCtx {
 struct DosaLayout {
   size_t ctx, rep_q, rep_w, rep_vis, rep_scores, rep_ids, counts, seeds, seed_mask, seed_keys,
       seed_scores, stat_cnt, stat_sum, top_idx, top_score, plan_a, plan_w, plan_c, knorm, bitmap,
-      surv_ids, surv_cnt, row_fb, kept_score, kept_id, kept_cnt, fb_list, fb_scores, total;
+      surv_ids, surv_cnt, row_fb, kept_score, kept_id, kept_cnt, fb_list, fb_scores, topk_ws,
+      topk_ws_bytes, total;
 };
 
 static size_t au(size_t x) { return (x + 255) / 256 * 256; }
@@ -98,6 +99,18 @@ static DosaLayout dosa_layout(int32_t n_q, int32_t H, int32_t D, int64_t n_k, in
   L.kept_cnt = take(nq * 4);
   L.fb_list = take(nq * 4);
   L.fb_scores = take(nq * nk * 4);
+  // candidate lists of the chunked top-K, shared by its three uses (the
+  // representative rows, the seed rows and the exact-path rows run one
+  // after the other)
+  {
+    size_t w = topk_workspace_bytes(R, nk, p->rep_topk);
+    const size_t w2 = topk_workspace_bytes(nq, ns, topk);
+    const size_t w3 = topk_workspace_bytes(nq, nk, topk);
+    w = w2 > w ? w2 : w;
+    w = w3 > w ? w3 : w;
+    L.topk_ws_bytes = w;
+    L.topk_ws = take(w);
+  }
   L.total = o;
   return L;
 }
@@ -801,6 +814,7 @@ static hipError_t run_dosa(const uint16_t* q, const uint16_t* k, const float* w,
     ta.scores = F(L.rep_scores); ta.stride = n_k; ta.vis_len = I(L.rep_vis);
     ta.k_row_offset = nullptr; ta.n_k = n_k; ta.max_vis = n_k; ta.n_rows = R;
     ta.K = p->rep_topk; ta.out_idx = I(L.rep_ids); ta.out_score = nullptr;
+    ta.workspace = ws + L.topk_ws; ta.workspace_bytes = L.topk_ws_bytes;
     e = launch_topk(ta, st);
     if (e != hipSuccess) return e;
     SI_TRY((dosa_count, dim3(grid_for((int64_t)R * p->rep_topk, 256)), dim3(256), 0, st,
@@ -819,6 +833,7 @@ static hipError_t run_dosa(const uint16_t* q, const uint16_t* k, const float* w,
     ta.scores = F(L.seed_scores); ta.stride = ns; ta.vis_len = nullptr; ta.k_row_offset = nullptr;
     ta.n_k = ns; ta.max_vis = ns; ta.n_rows = n_q; ta.K = topk; ta.out_idx = I(L.top_idx);
     ta.out_score = F(L.top_score); ta.id_map = I(L.seeds);
+    ta.workspace = ws + L.topk_ws; ta.workspace_bytes = L.topk_ws_bytes;
     hipError_t e = launch_topk(ta, st);
     if (e != hipSuccess) return e;
   }
@@ -852,6 +867,7 @@ static hipError_t run_dosa(const uint16_t* q, const uint16_t* k, const float* w,
     ta.scores = F(L.fb_scores); ta.stride = n_k; ta.vis_len = vis; ta.k_row_offset = nullptr;
     ta.n_k = n_k; ta.max_vis = n_k; ta.n_rows = n_q; ta.K = topk; ta.out_idx = out_idx;
     ta.out_score = out_score; ta.row_list = I(L.fb_list); ta.row_count = &ctx->n_fallback;
+    ta.workspace = ws + L.topk_ws; ta.workspace_bytes = L.topk_ws_bytes;
     e = launch_topk(ta, st);
     if (e != hipSuccess) return e;
   }
