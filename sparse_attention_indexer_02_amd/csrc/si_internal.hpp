@@ -59,6 +59,7 @@ __device__ __forceinline__ int64_t visible_len(const int32_t* vis_len, const int
 extern "C" __device__ int __ockl_wfscan_add_i32(int, bool);
 extern "C" __device__ unsigned __ockl_wfred_max_u32(unsigned);
 extern "C" __device__ unsigned __ockl_wfred_min_u32(unsigned);
+extern "C" __device__ unsigned __ockl_wfred_or_u32(unsigned);
 
 __device__ __forceinline__ int wave_incl_scan(int x) { return __ockl_wfscan_add_i32(x, true); }
 

@@ -8,9 +8,10 @@
 // below s), when that rank is < B.  Only those <= B slots are written.
 //
 // The segment of an in-range entry, floor(x S_eff / L), comes from an fp32
-// quotient estimate corrected once each way with exact 64-bit integer
-// arithmetic (the estimate is within 1 of the true floor: the quotient is
-// below 64 and the relative error of the estimate is a few 2^-24).
+// quotient estimate corrected once each way with exact integer arithmetic
+// (the estimate is within 1 of the true floor: the quotient is below 64 and
+// the relative error of the estimate is a few 2^-24); rows with L < 2^26
+// do it in 32 bits, longer ones in 64.
 #include "si_internal.hpp"
 
 namespace si {
@@ -37,6 +38,25 @@ __device__ __forceinline__ uint64_t seg_bit(int32_t x, uint32_t L, uint32_t S, u
   return 1ull << seg;
 }
 
+// The same segment for rows with L < 2^26, where x * S_eff < 2^32: the
+// product, the estimate's back-multiplication and the remainder all fit 32
+// bits (est * L <= num + L < 2^32), so the correction needs no 64-bit math.
+__device__ __forceinline__ uint64_t seg_bit32(int32_t x, uint32_t L, uint32_t S, uint32_t Se,
+                                              float rcpL) {
+  const uint32_t ux = (uint32_t)x;
+  uint32_t seg;
+  if (ux >= L) {
+    seg = (Se == S) ? S - 1 : (ux < S - 1 ? ux : S - 1);
+  } else {
+    const uint32_t num = ux * Se;
+    uint32_t est = (uint32_t)((float)num * rcpL);
+    const int32_t rem = (int32_t)(num - est * L);
+    est = rem < 0 ? est - 1 : (rem >= (int32_t)L ? est + 1 : est);
+    seg = est;
+  }
+  return x < 0 ? 0ull : 1ull << seg;
+}
+
 __global__ __launch_bounds__(kWitThreads) void witness_merge(int32_t* __restrict__ idx, int rows,
                                                              int topk,
                                                              const int32_t* __restrict__ lens,
@@ -54,7 +74,27 @@ __global__ __launch_bounds__(kWitThreads) void witness_merge(int32_t* __restrict
   uint64_t occ = 0ull;
   const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
   int t0 = 0;
-  if (vec) {
+  if (vec && L < (1u << 26)) {
+    // 16-byte loads, four rounds of loads in flight before their use
+    const int nv = topk >> 2;
+    const int4* rv = reinterpret_cast<const int4*>(row);
+    int i = lane;
+    for (; i + 192 < nv; i += 256) {
+      int4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = rv[i + 64 * u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        occ |= seg_bit32(x[u].x, L, S, Se, rcpL) | seg_bit32(x[u].y, L, S, Se, rcpL) |
+               seg_bit32(x[u].z, L, S, Se, rcpL) | seg_bit32(x[u].w, L, S, Se, rcpL);
+    }
+    for (; i < nv; i += 64) {
+      const int4 x = rv[i];
+      occ |= seg_bit32(x.x, L, S, Se, rcpL) | seg_bit32(x.y, L, S, Se, rcpL) |
+             seg_bit32(x.z, L, S, Se, rcpL) | seg_bit32(x.w, L, S, Se, rcpL);
+    }
+    t0 = nv << 2;
+  } else if (vec) {
     const int nv = topk >> 2;
     const int4* rv = reinterpret_cast<const int4*>(row);
     for (int i = lane; i < nv; i += 64) {
@@ -65,13 +105,8 @@ __global__ __launch_bounds__(kWitThreads) void witness_merge(int32_t* __restrict
     t0 = nv << 2;
   }
   for (int t = t0 + lane; t < topk; t += 64) occ |= seg_bit(row[t], L, S, Se, rcpL);
-  uint32_t lo = (uint32_t)occ, hi = (uint32_t)(occ >> 32);
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    lo |= (uint32_t)__shfl_xor((int)lo, o, 64);
-    hi |= (uint32_t)__shfl_xor((int)hi, o, 64);
-  }
-  occ = ((uint64_t)hi << 32) | lo;
+  occ = ((uint64_t)__ockl_wfred_or_u32((uint32_t)(occ >> 32)) << 32) |
+        __ockl_wfred_or_u32((uint32_t)occ);
 
   const bool empty = (uint32_t)lane < Se && !((occ >> lane) & 1ull);
   const uint64_t emask = __ballot(empty);
