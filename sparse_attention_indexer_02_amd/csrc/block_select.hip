@@ -128,6 +128,135 @@ __global__ __launch_bounds__(kBlkThreads) void block_max(BlockArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// block_max for 128-position blocks and D <= 128 (the MiniMax-M3 shape):
+// register-tiled VALU dots.  A workgroup owns a tile of 64 rows (flattened
+// (query, head) pairs) and a run of kBmRun blocks.  The tile's q sits in
+// LDS transposed [d][row]; each block's keys are staged 16 d at a time,
+// transposed [d][position].  Thread t computes rows 8 (t / 32) .. +7 for
+// positions 4 (t % 32) .. +3 of the block: per d step three 16-byte LDS
+// reads feed 32 separately rounded products and 32 adds, in d order from +0
+// exactly as the scalar definition.  Block maxima: over the thread's 4
+// positions, then across the 32 lanes sharing the rows.
+// ---------------------------------------------------------------------------
+constexpr int kBmRows = 64;
+constexpr int kBmPos = 128;
+constexpr int kBmDC = 16;
+constexpr int kBmMaxD = 128;
+constexpr int kBmRun = 32;  // blocks per workgroup
+
+__global__ __launch_bounds__(256) void block_max128(BlockArgs a, int runs) {
+  __shared__ __attribute__((aligned(16))) float qs[kBmMaxD][kBmRows];
+  __shared__ __attribute__((aligned(16))) float ks[2][kBmDC][kBmPos];
+  __shared__ int64_t rpos[kBmRows];
+  __shared__ int64_t tile_blocks;
+  const int t = threadIdx.x;
+  const int tile = (int)(blockIdx.x / runs), run = (int)(blockIdx.x % runs);
+  const int64_t nrows = (int64_t)a.n_q * a.H;
+  const int64_t row0 = (int64_t)tile * kBmRows;
+  const int D = a.D;
+  if (t == 0) tile_blocks = 0;
+  __syncthreads();
+  if (t < kBmRows) {
+    const int64_t row = row0 + t;
+    int64_t p = -1;
+    if (row < nrows) p = a.qpos[row / a.H];
+    rpos[t] = p;
+    const int64_t nb = n_blocks_of(p, a.n_pos, a.bs);
+    atomicMax(reinterpret_cast<unsigned long long*>(&tile_blocks), (unsigned long long)nb);
+  }
+  __syncthreads();
+  const int64_t b_lo = (int64_t)run * kBmRun;
+  const int64_t b_hi = tile_blocks < b_lo + kBmRun ? tile_blocks : b_lo + kBmRun;
+  if (b_lo >= b_hi) return;  // uniform: no row of the tile sees these blocks
+  // q tile, transposed
+  for (int e = t; e < kBmRows * D; e += 256) {
+    const int row = e / D, d = e - row * D;
+    const int64_t grow = row0 + row;
+    qs[d][row] = grow < nrows ? a.q[grow * D + d] : 0.0f;
+  }
+  const int rg = t >> 5, pg = t & 31;
+  int64_t myp[8], mynb[8];  // the rows' query positions and visible block counts
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    myp[i] = rpos[8 * rg + i];
+    mynb[i] = n_blocks_of(myp[i], a.n_pos, a.bs);
+  }
+  const int nchunk = (D + kBmDC - 1) / kBmDC;
+  // key staging: thread t loads position t / 2, d's (t & 1) * 8 .. +7 of the chunk
+  const int sp = t >> 1, sd = (t & 1) * 8;
+  // fetch a chunk into registers before the compute, write it to LDS after
+  float kr[8];
+  auto fetch = [&](int64_t b, int c) {
+    const int64_t pos = b * kBmPos + sp;
+    const int d0 = c * kBmDC + sd;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = d0 + j;
+      kr[j] = (pos < a.n_pos && d < D) ? a.k[pos * D + d] : 0.0f;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ks[buf][sd + j][sp] = kr[j];
+  };
+  __syncthreads();
+  for (int64_t b = b_lo; b < b_hi; ++b) {
+    float acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;  // +0 start
+    fetch(b, 0);
+    stash(0);
+    __syncthreads();
+    for (int c = 0; c < nchunk; ++c) {
+      const int buf = c & 1;
+      if (c + 1 < nchunk) fetch(b, c + 1);
+      const int dn = (D - c * kBmDC) < kBmDC ? (D - c * kBmDC) : kBmDC;
+      auto dstep = [&](int dd) {
+        const float4 qa = *reinterpret_cast<const float4*>(&qs[c * kBmDC + dd][8 * rg]);
+        const float4 qb = *reinterpret_cast<const float4*>(&qs[c * kBmDC + dd][8 * rg + 4]);
+        const float4 kv = *reinterpret_cast<const float4*>(&ks[buf][dd][4 * pg]);
+        const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+        const float kk[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float prod = qv[i] * kk[j];
+            acc[i][j] = acc[i][j] + prod;
+          }
+      };
+      if (dn == kBmDC) {  // whole chunk: unrolled, so the LDS reads run ahead
+#pragma unroll
+        for (int dd = 0; dd < kBmDC; ++dd) dstep(dd);
+      } else {
+        for (int dd = 0; dd < dn; ++dd) dstep(dd);
+      }
+      // buffer buf ^ 1 was last read in chunk c - 1, before the previous barrier
+      if (c + 1 < nchunk) stash(buf ^ 1);
+      __syncthreads();
+    }
+    // block maxima over the visible positions (max is exact in any order)
+    const int64_t pos0 = b * kBmPos + 4 * pg;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t pos = pos0 + j;
+        if (pos < a.n_pos && pos <= myp[i] && acc[i][j] > m) m = acc[i][j];
+      }
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o, 64));
+      const int64_t row = row0 + 8 * rg + i;
+      if (pg == 0 && row < nrows && b < mynb[i])
+        a.bscore[row * a.max_blocks + b] = m;
+    }
+  }
+}
+
 constexpr int kSelThreads = 256;
 
 __global__ __launch_bounds__(kSelThreads) void block_select(BlockArgs a) {
@@ -217,12 +346,20 @@ hipError_t launch_block_select(const float* q, const float* k, const int64_t* qp
   a.max_blocks = (n_pos + bs - 1) / bs;
   a.qt = H >= kBlkRows ? 1 : kBlkRows / H;
   if (n_q == 0) return hipSuccess;
-  const int64_t tiles = (n_q + a.qt - 1) / a.qt;
-  if (tiles * a.max_blocks > 0) {
-    hipLaunchKernelGGL(block_max, dim3((unsigned)(tiles * a.max_blocks)), dim3(kBlkThreads), 0,
-                       st, a);
+  if (bs == kBmPos && D <= kBmMaxD && a.max_blocks > 0) {
+    const int64_t tiles = ((int64_t)n_q * H + kBmRows - 1) / kBmRows;
+    const int runs = (int)((a.max_blocks + kBmRun - 1) / kBmRun);
+    hipLaunchKernelGGL(block_max128, dim3((unsigned)(tiles * runs)), dim3(256), 0, st, a, runs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  } else {
+    const int64_t tiles = (n_q + a.qt - 1) / a.qt;
+    if (tiles * a.max_blocks > 0) {
+      hipLaunchKernelGGL(block_max, dim3((unsigned)(tiles * a.max_blocks)), dim3(kBlkThreads), 0,
+                         st, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   hipLaunchKernelGGL(block_select, dim3((unsigned)((int64_t)n_q * H)), dim3(kSelThreads), 0, st,
                      a);
