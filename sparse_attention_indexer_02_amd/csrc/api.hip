@@ -140,15 +140,14 @@ si_status idx_score_topk(const void* q, si_dtype q_dtype, const void* k, si_dtyp
   sa.scores = reinterpret_cast<float*>(workspace);
   const size_t cand_off = (score_ws_bytes(n_q, max_vis) + 255) & ~(size_t)255;
 
-  hipError_t e = launch_score(sa, stream);
-  if (e != hipSuccess) return SI_ERR_DEVICE;
   TopkArgs ta;
   ta.scores = sa.scores; ta.stride = max_vis; ta.vis_len = vis_len; ta.k_row_offset = k_row_offset;
   ta.n_k = n_k; ta.max_vis = max_vis; ta.n_rows = n_q; ta.K = topk; ta.out_idx = out_idx;
   ta.out_score = out_score; ta.id_map = nullptr;
   ta.workspace = static_cast<unsigned char*>(workspace) + cand_off;
   ta.workspace_bytes = workspace_bytes - cand_off;
-  e = launch_topk(ta, stream);
+  hipError_t e = launch_score(sa, stream);
+  if (e == hipSuccess) e = launch_topk(ta, stream);
   return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
 }
 

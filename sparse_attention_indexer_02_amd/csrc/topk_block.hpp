@@ -1,0 +1,468 @@
+// Per-row top-K with one 256-thread workgroup and the row in registers,
+// for rows of at most 8192 scores and K <= 2048 (the block kernel of the
+// top-K stage and its chunk passes).
+#pragma once
+
+#include "si_internal.hpp"
+
+namespace si {
+
+// ---------------------------------------------------------------------------
+// Rows of at most 8192 scores, K <= 2048: one 256-thread workgroup per row,
+// thread t owning positions [32 t, 32 t + 32) in registers (16-byte loads),
+// so index order is thread order.
+//  A. load (a NaN score is taken as -inf) and the row's value range;
+//  B. histogram over 4096 bins linear in score value over [vmin, vmax];
+//  C. scan from the top bin: the bin b1 holding the K-th item, and per bin
+//     the packed (output offset << 16 | selected count);
+//  D. the exact K-th value T inside b1: every b1 item counts the b1 items
+//     above it when b1 is small, else a radix select on the key bits of
+//     b1's items picks T;
+//  E. the selected items (> T, then the lowest-index ones == T) are
+//     scattered grouped by bin; an item's output slot is its bin's offset
+//     plus the number of same-bin items ahead of it under (score desc,
+//     index asc).  The ordered row is staged in LDS and written coalesced.
+//     If some bin holds more than kCrowd selected items (heavy ties, very
+//     uneven scores) the row is ordered by a bitonic sort instead.
+// ---------------------------------------------------------------------------
+constexpr int kBT = 256;             // threads per row
+constexpr int kBPer = 32;            // positions per thread
+constexpr int kBN = kBT * kBPer;     // 8192
+constexpr int kBK = 2048;            // largest K
+constexpr int kBItems = kBK / kBT;   // ordered items per thread
+constexpr int kBins = 4096;          // value bins
+constexpr int kBinsPer = kBins / kBT;
+constexpr int kBrute = 256;          // largest b1 ranked item by item
+constexpr int kCrowd = 64;           // largest per-bin count ranked by scanning the bin
+
+struct alignas(16) BlockSmem {
+  uint32_t bins[kBins];  // histogram, then packed (cursor << 16 | selected count)
+  union {
+    uint64_t comp[kBK];     // selected (key << 32 | ~position) grouped by bin,
+                            // then the ordered row
+    uint32_t sub[2048];     // refine histogram
+    uint32_t list[kBrute];  // b1's values
+  } x;
+};
+
+// Owner search over nb bins from the top (thread t owns nb/kBT consecutive
+// bins, highest first): the bin holding the want-th item from the top, the
+// items above it and its count.  get(b) reads bin b's count.
+template <class Get>
+__device__ __forceinline__ void find_from_top(Get get, int nb, int want, int* red, int* bin,
+                                              int* above, int* count) {
+  const int t = threadIdx.x;
+  const int per = nb / kBT;
+  const int first = nb - 1 - t * per;
+  int c = 0;
+  for (int j = 0; j < per; ++j) c += (int)get(first - j);
+  int tot;
+  const int ab = block_excl_scan<kBT>(c, red, &tot);
+  if (ab < want && ab + c >= want) {
+    int acc = ab;
+    for (int j = 0; j < per; ++j) {
+      const int h = (int)get(first - j);
+      if (acc + h >= want) {
+        red[kBT / 64] = first - j;
+        red[kBT / 64 + 1] = acc;
+        red[kBT / 64 + 2] = h;
+        break;
+      }
+      acc += h;
+    }
+  }
+  __syncthreads();
+  *bin = red[kBT / 64];
+  *above = red[kBT / 64 + 1];
+  *count = red[kBT / 64 + 2];
+  __syncthreads();
+}
+
+struct TopkSmem {
+  BlockSmem sm;
+  int red[kBT / 64 + 8];
+  float fred[2][kBT / 64];
+  uint32_t wred[kBT / 64];
+  int lcount;
+};
+
+// One row (or one chunk of a row) with the 256 threads of the calling
+// workgroup; every thread must call it (it synchronises the workgroup).
+__device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy, TopkSmem& S) {
+  BlockSmem& sm = S.sm;
+  int* red = S.red;
+  float (*fred)[kBT / 64] = S.fred;
+  uint32_t* wred = S.wred;
+  int& lcount = S.lcount;
+  const int t = (int)threadIdx.x;
+  const int lane = t & 63, wid = t >> 6;
+  int64_t off;
+  int64_t n64 =
+      a.vis_len ? visible_len(a.vis_len, a.k_row_offset, r, a.n_k, a.max_vis, &off) : a.max_vis;
+  const int K = a.K;
+  // chunk mode: this block takes positions [start, start + chunk) of the row
+  // and writes its ordered top-K at y K of the output row; an empty chunk
+  // writes nothing (the next level never reads it)
+  const int64_t start = a.chunk > 0 ? (int64_t)cy * a.chunk : 0;
+  if (a.chunk > 0) {
+    n64 -= start;
+    if (n64 <= 0) return;
+    n64 = n64 < a.chunk ? n64 : a.chunk;
+  }
+  const int n = (int)(n64 < kBN ? n64 : kBN);
+  const int cnt = n < K ? n : K;
+  const float* row = a.scores + (int64_t)r * a.stride + start;
+  const int64_t ostride = a.out_stride > 0 ? a.out_stride : K;
+  const int64_t obase = (int64_t)r * ostride + (a.chunk > 0 ? (int64_t)cy * K : 0);
+  int32_t* oi = a.out_idx + obase;
+  float* os = a.out_score ? a.out_score + obase : nullptr;
+  const int32_t* idmap = a.id_map ? a.id_map + (int64_t)r * a.id_map_stride + start : nullptr;
+  const int p0 = kBPer * t;
+  if (n <= 0) {
+    for (int q = t; q < K; q += kBT) {
+      oi[q] = -1;
+      if (os) os[q] = -__builtin_inff();
+    }
+    return;
+  }
+  const bool select = n > K;
+  // bit i: position p0 + i is visible.  Only the thread holding the row's
+  // end (and threads past it) has invalid positions; it takes the slow
+  // paths, every other thread the branch-free ones.
+  const int nv = n - p0;
+  const uint32_t vm = nv >= kBPer ? 0xFFFFFFFFu : (nv <= 0 ? 0u : (1u << nv) - 1u);
+  const bool full = vm == 0xFFFFFFFFu;
+
+  // A. load.  A NaN score is taken as -inf (its order is unspecified; this
+  //    makes every comparison below a total preorder on floats, -0 == +0).
+  for (int i = t; i < kBins; i += kBT) sm.bins[i] = 0u;
+  if (t == 0) lcount = 0;
+  auto clean = [](float v) { return v == v ? v : -__builtin_inff(); };
+  float x[kBPer];
+  {
+    const float* rp = row + p0;
+    const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+    if (vec && full) {  // 16-byte loads, all in flight at once
+#pragma unroll
+      for (int v = 0; v < kBPer / 4; ++v) {
+        const float4 q = reinterpret_cast<const float4*>(rp)[v];
+        x[4 * v + 0] = q.x;
+        x[4 * v + 1] = q.y;
+        x[4 * v + 2] = q.z;
+        x[4 * v + 3] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kBPer; ++i) x[i] = ((vm >> i) & 1u) ? rp[i] : 0.0f;
+    }
+  }
+  float vlo = __builtin_inff(), vhi = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < kBPer; ++i) x[i] = clean(x[i]);
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) {
+      vlo = __builtin_fminf(vlo, x[i]);
+      vhi = __builtin_fmaxf(vhi, x[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i)
+      if ((vm >> i) & 1u) {
+        vlo = __builtin_fminf(vlo, x[i]);
+        vhi = __builtin_fmaxf(vhi, x[i]);
+      }
+  }
+  {
+    const uint32_t klo = __ockl_wfred_min_u32(order_key(vlo));
+    const uint32_t khi = __ockl_wfred_max_u32(order_key(vhi));
+    if (lane == 0) {
+      fred[0][wid] = key_to_float(klo);
+      fred[1][wid] = key_to_float(khi);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kBT / 64; ++i) {
+    vlo = __builtin_fminf(vlo, fred[0][i]);
+    vhi = __builtin_fmaxf(vhi, fred[1][i]);
+  }
+
+  // B. histogram over kBins bins linear in score value over [vmin, vmax]:
+  //    bin(v) = (v - vmin) * scale rounded down, scale = (kBins - 0.01) /
+  //    (vmax - vmin), so bin(vmax) < kBins after rounding.  bin() is
+  //    monotone, so every item of a higher bin is greater than every item
+  //    of a lower one.  A row without a finite positive span (all equal,
+  //    infinities) puts everything in bin 0 and takes the general paths.
+  //    (readfirstlane takes an int: broadcast the bit patterns.)
+  const float vmin = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vlo)));
+  const float vmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vhi)));
+  const float span = vmax - vmin;
+  const float scale0 = ((float)kBins - 0.01f) / span;
+  const bool flat = !(span > 0.0f) || !(span <= 3.0e38f) || !(scale0 <= 3.0e38f);
+  const float scale = flat ? 0.0f : scale0;
+  // the 32 bins are computed once and kept packed, two per register
+  // (positions past the row's end hold vmin, so every conversion is in range)
+  if (!full) {
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) x[i] = ((vm >> i) & 1u) ? x[i] : vmin;
+  }
+  uint32_t pk[kBPer / 2];
+  if (flat) {
+#pragma unroll
+    for (int j = 0; j < kBPer / 2; ++j) pk[j] = 0u;
+  } else {
+#pragma unroll
+    for (int j = 0; j < kBPer / 2; ++j)
+      pk[j] = (uint32_t)((x[2 * j] - vmin) * scale) |
+              ((uint32_t)((x[2 * j + 1] - vmin) * scale) << 16);
+  }
+  auto bin_of = [&](int i) -> uint32_t { return (pk[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu; };
+  auto bin = [&](float v) -> uint32_t { return flat ? 0u : (uint32_t)((v - vmin) * scale); };
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) atomicAdd(&sm.bins[bin_of(i)], 1u);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i)
+      if ((vm >> i) & 1u) atomicAdd(&sm.bins[bin_of(i)], 1u);
+  }
+  __syncthreads();
+
+  // C. b1 and the packed per-bin (offset << 16 | selected count), from the
+  //    top; thread t owns the kBinsPer bins below kBins - kBinsPer t
+  const int want = select ? K : n;
+  int b1, ab1, in_bin;
+  {
+    const int top = kBins - 1 - kBinsPer * t;  // highest bin of this thread
+    uint32_t c[kBinsPer];
+#pragma unroll
+    for (int v = 0; v < kBinsPer / 4; ++v) {
+      const uint4 q = *reinterpret_cast<const uint4*>(&sm.bins[top - 3 - 4 * v]);
+      c[4 * v + 0] = q.w;
+      c[4 * v + 1] = q.z;
+      c[4 * v + 2] = q.y;
+      c[4 * v + 3] = q.x;
+    }
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < kBinsPer; ++j) sum += (int)c[j];
+    int tot;
+    const int ab = block_excl_scan<kBT>(sum, red, &tot);
+    if (ab < want && ab + sum >= want) {
+      int acc = ab;
+#pragma unroll
+      for (int j = 0; j < kBinsPer; ++j) {
+        if (acc < want && acc + (int)c[j] >= want) {
+          red[kBT / 64] = top - j;
+          red[kBT / 64 + 1] = acc;
+          red[kBT / 64 + 2] = (int)c[j];
+        }
+        acc += (int)c[j];
+      }
+    }
+    __syncthreads();
+    b1 = red[kBT / 64];
+    ab1 = red[kBT / 64 + 1];
+    in_bin = red[kBT / 64 + 2];
+    // selected counts: all of every bin above b1, want - ab1 of b1; output
+    // offsets are the exclusive prefix from the top
+    uint32_t o = (uint32_t)ab, crowd = 0u;
+#pragma unroll
+    for (int j = 0; j < kBinsPer; ++j) {
+      const int b = top - j;
+      const uint32_t sel = b > b1 ? c[j] : (b == b1 ? (uint32_t)(want - ab1) : 0u);
+      const uint32_t cj = c[j];
+      c[j] = (o << 16) | sel;
+      crowd = sel > crowd ? sel : crowd;
+      o += cj;
+    }
+#pragma unroll
+    for (int v = 0; v < kBinsPer / 4; ++v)
+      *reinterpret_cast<uint4*>(&sm.bins[top - 3 - 4 * v]) =
+          make_uint4(c[4 * v + 3], c[4 * v + 2], c[4 * v + 1], c[4 * v + 0]);
+    crowd = __ockl_wfred_max_u32(crowd);
+    if (lane == 0) wred[wid] = crowd;
+  }
+  __syncthreads();
+  uint32_t crowd = 0u;
+#pragma unroll
+  for (int i = 0; i < kBT / 64; ++i) crowd = wred[i] > crowd ? wred[i] : crowd;
+
+  // D. the exact threshold value T inside b1
+  float thr = 0.0f;
+  int n_gt = 0, n_eq = 0;
+  if (select) {
+    const int need = K - ab1;  // rank of T among b1's items, >= 1
+    uint32_t inb = 0u;         // which of this thread's items lie in b1
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) inb |= ((int)bin_of(i) == b1) ? (1u << i) : 0u;
+    inb &= vm;
+    if (in_bin <= kBrute) {
+      // b1 holds few items: each position is a uniform skip unless some
+      // lane of the wave has one there (the mask is re-derived per position
+      // so the compiler does not hold 32 of them)
+#pragma unroll
+      for (int i = 0; i < kBPer; ++i) {
+        asm volatile("" : "+v"(inb));
+        if ((inb >> i) & 1u) sm.x.list[atomicAdd(&lcount, 1)] = __float_as_uint(x[i]);
+      }
+      __syncthreads();
+      if (t < in_bin) {
+        const float me = __uint_as_float(sm.x.list[t]);
+        int g = 0, e = 0;
+        for (int j = 0; j < in_bin; ++j) {
+          const float v = __uint_as_float(sm.x.list[j]);
+          g += v > me ? 1 : 0;
+          e += v == me ? 1 : 0;
+        }
+        if (g < need && need <= g + e) {  // every holder of T writes the same values
+          red[kBT / 64 + 3] = (int)__float_as_uint(me);
+          red[kBT / 64 + 4] = g;
+          red[kBT / 64 + 5] = e;
+        }
+      }
+      __syncthreads();
+      thr = __uint_as_float((uint32_t)red[kBT / 64 + 3]);
+      n_gt = ab1 + red[kBT / 64 + 4];
+      n_eq = red[kBT / 64 + 5];
+    } else {
+      // radix select among b1's items on the key digits 11/11/10; this rare
+      // path re-reads b1's scores (from cache) rather than tying up the
+      // register-resident row
+      uint32_t prefix = 0u, pmask = 0u;
+      int rank = need, above = ab1, count = in_bin;
+#pragma unroll 1
+      for (int level = 0; level < 3; ++level) {
+        const int sh = level == 0 ? 21 : (level == 1 ? 10 : 0);
+        const uint32_t dmask = level == 2 ? 1023u : 2047u;
+        for (int i = t; i < 2048; i += kBT) sm.x.sub[i] = 0u;
+        __syncthreads();
+        asm volatile("" : "+v"(inb));
+        for (uint32_t mb = inb; mb != 0u; mb &= mb - 1u) {
+          const uint32_t k = order_key(clean(row[p0 + __builtin_ctz(mb)]));
+          if ((k & pmask) == prefix) atomicAdd(&sm.x.sub[(k >> sh) & dmask], 1u);
+        }
+        __syncthreads();
+        int dig, ab;
+        find_from_top([&](int b) { return sm.x.sub[b]; }, 2048, rank, red, &dig, &ab, &count);
+        rank -= ab;
+        above += ab;
+        prefix |= (uint32_t)dig << sh;
+        pmask |= dmask << sh;
+      }
+      thr = key_to_float(prefix);
+      n_gt = above;
+      n_eq = count;
+    }
+  }
+
+  // E. scatter the selected items grouped by bin (cursor = packed high half)
+  const int need_eq = select ? K - n_gt : 0;
+  {
+    // selection mask: everything (no selection), or > T plus the first
+    // `take` positions == T of this thread in index order
+    uint32_t selm = vm;
+    if (select) {
+      uint32_t gtm = 0u, eqm = 0u;
+#pragma unroll
+      for (int i = 0; i < kBPer; ++i) {
+        gtm |= x[i] > thr ? (1u << i) : 0u;
+        eqm |= x[i] == thr ? (1u << i) : 0u;
+      }
+      gtm &= vm;
+      eqm &= vm;
+      const int c_eq = __builtin_popcount(eqm);
+      int eq_before = 0, tot;
+      if (need_eq < n_eq) eq_before = block_excl_scan<kBT>(c_eq, red, &tot);  // uniform branch
+      int take = need_eq - eq_before;
+      take = take < 0 ? 0 : (take > c_eq ? c_eq : take);
+      for (int k = c_eq - take; k > 0; --k) eqm &= ~(1u << (31 - __builtin_clz(eqm)));  // drop the highest
+      selm = gtm | eqm;
+    }
+    // eight returning cursor atomics in flight, then their eight stores
+#pragma unroll
+    for (int c = 0; c < kBPer / 8; ++c) {
+      uint32_t pos[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = 8 * c + k;
+        pos[k] = 0u;
+        if ((selm >> i) & 1u) pos[k] = atomicAdd(&sm.bins[bin_of(i)], 0x10000u) >> 16;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = 8 * c + k;
+        if ((selm >> i) & 1u) {
+          // orderable key (-0 folded onto +0) into a fresh register: the
+          // 64-bit store takes an aligned pair, and a copy keeps the
+          // compiler from pinning all 32 items to pairs
+          uint32_t kc;
+          asm volatile("v_mov_b32 %0, %1" : "=v"(kc) : "v"(order_key(x[i])));
+          sm.x.comp[pos[k]] = ((uint64_t)kc << 32) | (uint32_t)(~(uint32_t)(p0 + i));
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  if (crowd <= (uint32_t)kCrowd) {
+    // rank inside the bin: after the scatter a bin's packed word is
+    // ((offset + count) << 16 | count).  The bin is scanned four entries per
+    // step with no branch in the step: four independent LDS reads (index
+    // clamped inside the list), then masked compares.
+    uint64_t it[kBItems];
+    uint32_t dst[kBItems];
+#pragma unroll
+    for (int m = 0; m < kBItems; ++m) {
+      const int q = kBItems * t + m;
+      it[m] = 0ull;
+      dst[m] = 0u;
+      if (q < cnt) {
+        it[m] = sm.x.comp[q];
+        const uint32_t w = sm.bins[bin(key_to_float((uint32_t)(it[m] >> 32)))];
+        const uint32_t len = w & 0xFFFFu, s0 = (w >> 16) - len;
+        uint32_t rk = 0u;
+        for (uint32_t j = 0; j < len; j += 4) {
+          uint64_t v[4];
+#pragma unroll
+          for (uint32_t k = 0; k < 4; ++k) {
+            const uint32_t x2 = s0 + j + k;
+            v[k] = sm.x.comp[x2 < (uint32_t)kBK ? x2 : (uint32_t)kBK - 1u];
+          }
+#pragma unroll
+          for (uint32_t k = 0; k < 4; ++k)
+            rk += (uint32_t)(j + k < len) & (uint32_t)(v[k] > it[m]);
+        }
+        dst[m] = s0 + rk;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < kBItems; ++m)
+      if (kBItems * t + m < cnt) sm.x.comp[dst[m]] = it[m];
+    __syncthreads();
+  } else {
+    const int P = next_pow2(cnt);
+    for (int q = cnt + t; q < P; q += kBT) sm.x.comp[q] = 0ull;
+    __syncthreads();
+    bitonic_sort_desc<kBT>(sm.x.comp, P);
+  }
+
+  // coalesced output of the ordered row, then the padding.  Positions are
+  // < n by construction; the clamp only keeps an id_map lookup in bounds.
+  for (int q = t; q < K; q += kBT) {
+    if (q < cnt) {
+      const uint64_t c = sm.x.comp[q];
+      uint32_t p = ~(uint32_t)c;
+      p = p < (uint32_t)n ? p : 0u;
+      oi[q] = idmap ? idmap[p] : (int32_t)(start + p);
+      if (os) os[q] = key_to_float((uint32_t)(c >> 32));
+    } else {
+      oi[q] = -1;
+      if (os) os[q] = -__builtin_inff();
+    }
+  }
+}
+
+}  // namespace si
