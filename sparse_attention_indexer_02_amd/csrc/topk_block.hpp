@@ -8,9 +8,11 @@
 namespace si {
 
 // ---------------------------------------------------------------------------
-// Rows of at most 8192 scores, K <= 2048: one 256-thread workgroup per row,
-// thread t owning positions [32 t, 32 t + 32) in registers (16-byte loads),
-// so index order is thread order.
+// Rows of at most 8192 scores, K <= 2048: one 256-thread workgroup per row.
+// Thread t holds the float4 groups t, t + 256, ..., t + 1792 of the row
+// (positions 4 t + 1024 j + c), so each load instruction of the workgroup
+// reads 4 KB contiguous and a row of n scores keeps all four waves busy on
+// its first ceil(n / 1024) group rows (the rest are skipped uniformly).
 //  A. load (a NaN score is taken as -inf) and the row's value range;
 //  B. histogram over 4096 bins linear in score value over [vmin, vmax];
 //  C. scan from the top bin: the bin b1 holding the K-th item, and per bin
@@ -18,30 +20,42 @@ namespace si {
 //  D. the exact K-th value T inside b1: every b1 item counts the b1 items
 //     above it when b1 is small, else a radix select on the key bits of
 //     b1's items picks T;
-//  E. the selected items (> T, then the lowest-index ones == T) are
-//     scattered grouped by bin; an item's output slot is its bin's offset
-//     plus the number of same-bin items ahead of it under (score desc,
-//     index asc).  The ordered row is staged in LDS and written coalesced.
-//     If some bin holds more than kCrowd selected items (heavy ties, very
-//     uneven scores) the row is ordered by a bitonic sort instead.
+//  E. the selected items (> T, then the lowest-index ones == T, found with
+//     a position bitmap when T is tied) are scattered grouped by bin; an
+//     item's output slot is its bin's offset plus the number of same-bin
+//     items ahead of it under (score desc, index asc), counted over the bin
+//     four entries at a time (entries past the bin belong to lower bins or
+//     are zero, so they never count).  The ordered row is staged in LDS and
+//     written coalesced.  If some bin holds more than kCrowd selected items
+//     (heavy ties, very uneven scores) the row is ordered by a bitonic sort.
+// Staged items are 64-bit composites: order key << 32 | bin << 13 |
+// (8191 - position); composites compare as (score desc, index asc), and the
+// bin rides along so the rank step need not recompute it.
 // ---------------------------------------------------------------------------
-constexpr int kBT = 256;             // threads per row
-constexpr int kBPer = 32;            // positions per thread
-constexpr int kBN = kBT * kBPer;     // 8192
-constexpr int kBK = 2048;            // largest K
-constexpr int kBItems = kBK / kBT;   // ordered items per thread
-constexpr int kBins = 4096;          // value bins
+constexpr int kBT = 256;              // threads per row
+constexpr int kBPer = 32;             // positions per thread
+constexpr int kBN = kBT * kBPer;      // 8192
+constexpr int kBGroups = kBPer / 4;   // float4 groups per thread
+constexpr int kBStep = 4 * kBT;       // positions per group row
+constexpr int kBK = 2048;             // largest K
+constexpr int kBins = 4096;           // value bins
 constexpr int kBinsPer = kBins / kBT;
-constexpr int kBrute = 256;          // largest b1 ranked item by item
-constexpr int kCrowd = 64;           // largest per-bin count ranked by scanning the bin
+constexpr int kBrute = 256;           // largest b1 ranked item by item
+constexpr int kCrowd = 64;            // largest per-bin count ranked by scanning the bin
+constexpr int kPosBits = 13;          // positions < kBN
+constexpr uint32_t kPosMask = (1u << kPosBits) - 1u;
 
 struct alignas(16) BlockSmem {
   uint32_t bins[kBins];  // histogram, then packed (cursor << 16 | selected count)
   union {
-    uint64_t comp[kBK];     // selected (key << 32 | ~position) grouped by bin,
-                            // then the ordered row
-    uint32_t sub[2048];     // refine histogram
-    uint32_t list[kBrute];  // b1's values
+    uint64_t comp[kBK + 4];  // selected composites grouped by bin (+ 4 zero
+                             // entries past the last), then the ordered row
+    uint32_t sub[2048];      // refine histogram
+    uint32_t list[kBrute];   // b1's values
+    struct {
+      uint32_t bits[kBN / 32];  // positions holding T
+      uint32_t pre[kBN / 32];   // exclusive prefix of their popcounts
+    } eq;
   } x;
 };
 
@@ -117,7 +131,6 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   int32_t* oi = a.out_idx + obase;
   float* os = a.out_score ? a.out_score + obase : nullptr;
   const int32_t* idmap = a.id_map ? a.id_map + (int64_t)r * a.id_map_stride + start : nullptr;
-  const int p0 = kBPer * t;
   if (n <= 0) {
     for (int q = t; q < K; q += kBT) {
       oi[q] = -1;
@@ -126,12 +139,18 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
     return;
   }
   const bool select = n > K;
-  // bit i: position p0 + i is visible.  Only the thread holding the row's
-  // end (and threads past it) has invalid positions; it takes the slow
-  // paths, every other thread the branch-free ones.
-  const int nv = n - p0;
-  const uint32_t vm = nv >= kBPer ? 0xFFFFFFFFu : (nv <= 0 ? 0u : (1u << nv) - 1u);
-  const bool full = vm == 0xFFFFFFFFu;
+  // group rows [0, gfull) are visible everywhere, group row gfull (if
+  // < gused) partly; the rest hold nothing.  Bit 4 j + c of vm: position
+  // base + kBStep j + c is visible.
+  const int base = 4 * t;
+  const int gfull = n / kBStep;
+  const int gused = (n + kBStep - 1) / kBStep;
+  auto pos_of = [&](int i) { return base + kBStep * (i >> 2) + (i & 3); };
+  uint32_t vm = gfull >= kBGroups ? 0xFFFFFFFFu : ((1u << (4 * gfull)) - 1u);
+  if (gfull < kBGroups) {
+    const int nv = n - base - kBStep * gfull;
+    vm |= (nv >= 4 ? 0xFu : (nv <= 0 ? 0u : (1u << nv) - 1u)) << (4 * gfull);
+  }
 
   // A. load.  A NaN score is taken as -inf (its order is unspecified; this
   //    makes every comparison below a total preorder on floats, -0 == +0).
@@ -140,38 +159,48 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   auto clean = [](float v) { return v == v ? v : -__builtin_inff(); };
   float x[kBPer];
   {
-    const float* rp = row + p0;
+    const float* rp = row + base;
     const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
-    if (vec && full) {  // 16-byte loads, all in flight at once
 #pragma unroll
-      for (int v = 0; v < kBPer / 4; ++v) {
-        const float4 q = reinterpret_cast<const float4*>(rp)[v];
-        x[4 * v + 0] = q.x;
-        x[4 * v + 1] = q.y;
-        x[4 * v + 2] = q.z;
-        x[4 * v + 3] = q.w;
+    for (int j = 0; j < kBGroups; ++j) {
+      if (vec && j < gfull) {
+        const float4 q = *reinterpret_cast<const float4*>(rp + kBStep * j);
+        x[4 * j + 0] = q.x;
+        x[4 * j + 1] = q.y;
+        x[4 * j + 2] = q.z;
+        x[4 * j + 3] = q.w;
+      } else if (j < gused) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          x[4 * j + c] = ((vm >> (4 * j + c)) & 1u) ? rp[kBStep * j + c] : 0.0f;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[4 * j + c] = 0.0f;
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kBPer; ++i) x[i] = ((vm >> i) & 1u) ? rp[i] : 0.0f;
     }
   }
   float vlo = __builtin_inff(), vhi = -__builtin_inff();
 #pragma unroll
-  for (int i = 0; i < kBPer; ++i) x[i] = clean(x[i]);
-  if (full) {
+  for (int j = 0; j < kBGroups; ++j) {
+    if (j < gfull) {
 #pragma unroll
-    for (int i = 0; i < kBPer; ++i) {
-      vlo = __builtin_fminf(vlo, x[i]);
-      vhi = __builtin_fmaxf(vhi, x[i]);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kBPer; ++i)
-      if ((vm >> i) & 1u) {
-        vlo = __builtin_fminf(vlo, x[i]);
-        vhi = __builtin_fmaxf(vhi, x[i]);
+      for (int c = 0; c < 4; ++c) {
+        float& v = x[4 * j + c];
+        v = clean(v);
+        vlo = __builtin_fminf(vlo, v);
+        vhi = __builtin_fmaxf(vhi, v);
       }
+    } else if (j < gused) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float& v = x[4 * j + c];
+        v = clean(v);
+        if ((vm >> (4 * j + c)) & 1u) {
+          vlo = __builtin_fminf(vlo, v);
+          vhi = __builtin_fmaxf(vhi, v);
+        }
+      }
+    }
   }
   {
     const uint32_t klo = __ockl_wfred_min_u32(order_key(vlo));
@@ -201,31 +230,36 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   const float scale0 = ((float)kBins - 0.01f) / span;
   const bool flat = !(span > 0.0f) || !(span <= 3.0e38f) || !(scale0 <= 3.0e38f);
   const float scale = flat ? 0.0f : scale0;
-  // the 32 bins are computed once and kept packed, two per register
+  // the bins are computed once and kept packed, two per register
   // (positions past the row's end hold vmin, so every conversion is in range)
-  if (!full) {
-#pragma unroll
-    for (int i = 0; i < kBPer; ++i) x[i] = ((vm >> i) & 1u) ? x[i] : vmin;
-  }
   uint32_t pk[kBPer / 2];
-  if (flat) {
 #pragma unroll
-    for (int j = 0; j < kBPer / 2; ++j) pk[j] = 0u;
-  } else {
+  for (int j = 0; j < kBGroups; ++j) {
+    if (j < gused && !flat) {
+      if (j >= gfull) {
 #pragma unroll
-    for (int j = 0; j < kBPer / 2; ++j)
-      pk[j] = (uint32_t)((x[2 * j] - vmin) * scale) |
-              ((uint32_t)((x[2 * j + 1] - vmin) * scale) << 16);
+        for (int c = 0; c < 4; ++c) x[4 * j + c] = ((vm >> (4 * j + c)) & 1u) ? x[4 * j + c] : vmin;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        pk[2 * j + h] = (uint32_t)((x[4 * j + 2 * h] - vmin) * scale) |
+                        ((uint32_t)((x[4 * j + 2 * h + 1] - vmin) * scale) << 16);
+    } else {
+      pk[2 * j] = 0u;
+      pk[2 * j + 1] = 0u;
+    }
   }
   auto bin_of = [&](int i) -> uint32_t { return (pk[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu; };
-  auto bin = [&](float v) -> uint32_t { return flat ? 0u : (uint32_t)((v - vmin) * scale); };
-  if (full) {
 #pragma unroll
-    for (int i = 0; i < kBPer; ++i) atomicAdd(&sm.bins[bin_of(i)], 1u);
-  } else {
+  for (int j = 0; j < kBGroups; ++j) {
+    if (j < gfull) {
 #pragma unroll
-    for (int i = 0; i < kBPer; ++i)
-      if ((vm >> i) & 1u) atomicAdd(&sm.bins[bin_of(i)], 1u);
+      for (int c = 0; c < 4; ++c) atomicAdd(&sm.bins[bin_of(4 * j + c)], 1u);
+    } else if (j < gused) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((vm >> (4 * j + c)) & 1u) atomicAdd(&sm.bins[bin_of(4 * j + c)], 1u);
+    }
   }
   __syncthreads();
 
@@ -340,7 +374,7 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
         __syncthreads();
         asm volatile("" : "+v"(inb));
         for (uint32_t mb = inb; mb != 0u; mb &= mb - 1u) {
-          const uint32_t k = order_key(clean(row[p0 + __builtin_ctz(mb)]));
+          const uint32_t k = order_key(clean(row[pos_of((int)__builtin_ctz(mb))]));
           if ((k & pmask) == prefix) atomicAdd(&sm.x.sub[(k >> sh) & dmask], 1u);
         }
         __syncthreads();
@@ -357,90 +391,109 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
     }
   }
 
-  // E. scatter the selected items grouped by bin (cursor = packed high half)
-  const int need_eq = select ? K - n_gt : 0;
-  {
-    // selection mask: everything (no selection), or > T plus the first
-    // `take` positions == T of this thread in index order
-    uint32_t selm = vm;
-    if (select) {
-      uint32_t gtm = 0u, eqm = 0u;
+  // E. selection: everything visible (no selection), or > T plus the
+  //    need_eq lowest positions == T.  When T is tied beyond need_eq, the
+  //    positions holding T go into a bitmap whose word prefix counts give
+  //    each one its index-order rank among them.
+  uint32_t selm = vm;
+  if (select) {
+    const int need_eq = K - n_gt;
+    uint32_t gtm = 0u, eqm = 0u;
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) {
+      gtm |= x[i] > thr ? (1u << i) : 0u;
+      eqm |= x[i] == thr ? (1u << i) : 0u;
+    }
+    gtm &= vm;
+    eqm &= vm;
+    if (need_eq < n_eq) {  // uniform: T is tied past the K-th place
+      for (int i = t; i < kBN / 32; i += kBT) sm.x.eq.bits[i] = 0u;
+      __syncthreads();
+      // the four positions of group j share word (t >> 3) + 32 j
+#pragma unroll
+      for (int j = 0; j < kBGroups; ++j) {
+        const uint32_t g4 = (eqm >> (4 * j)) & 0xFu;
+        if (g4) atomicOr(&sm.x.eq.bits[(t >> 3) + 32 * j], g4 << (4 * (t & 7)));
+      }
+      __syncthreads();
+      int tot;
+      const uint32_t wbits = sm.x.eq.bits[t];  // kBN / 32 == kBT words
+      sm.x.eq.pre[t] = (uint32_t)block_excl_scan<kBT>(__builtin_popcount(wbits), red, &tot);
+      __syncthreads();
+      uint32_t keep = 0u;
 #pragma unroll
       for (int i = 0; i < kBPer; ++i) {
-        gtm |= x[i] > thr ? (1u << i) : 0u;
-        eqm |= x[i] == thr ? (1u << i) : 0u;
+        if ((eqm >> i) & 1u) {
+          const int p = pos_of(i);
+          const uint32_t w = sm.x.eq.bits[p >> 5];
+          const int rank = (int)sm.x.eq.pre[p >> 5] + __builtin_popcount(w & ((1u << (p & 31)) - 1u));
+          keep |= rank < need_eq ? (1u << i) : 0u;
+        }
       }
-      gtm &= vm;
-      eqm &= vm;
-      const int c_eq = __builtin_popcount(eqm);
-      int eq_before = 0, tot;
-      if (need_eq < n_eq) eq_before = block_excl_scan<kBT>(c_eq, red, &tot);  // uniform branch
-      int take = need_eq - eq_before;
-      take = take < 0 ? 0 : (take > c_eq ? c_eq : take);
-      for (int k = c_eq - take; k > 0; --k) eqm &= ~(1u << (31 - __builtin_clz(eqm)));  // drop the highest
-      selm = gtm | eqm;
+      eqm = keep;
+      __syncthreads();  // the bitmap area is reused by the scatter
     }
-    // eight returning cursor atomics in flight, then their eight stores
+    selm = gtm | eqm;
+  }
+
+  // F. scatter the selected items grouped by bin (cursor = packed high
+  //    half), eight returning cursor atomics in flight, then their stores;
+  //    the four entries past the last item are zeroed for the rank scan
+  if (t < 4) sm.x.comp[cnt + t] = 0ull;
 #pragma unroll
-    for (int c = 0; c < kBPer / 8; ++c) {
-      uint32_t pos[8];
+  for (int g = 0; g < kBGroups / 2; ++g) {
+    if (2 * g < gused) {
+      uint32_t slot[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int i = 8 * c + k;
-        pos[k] = 0u;
-        if ((selm >> i) & 1u) pos[k] = atomicAdd(&sm.bins[bin_of(i)], 0x10000u) >> 16;
+        const int i = 8 * g + k;
+        slot[k] = 0u;
+        if ((selm >> i) & 1u) slot[k] = atomicAdd(&sm.bins[bin_of(i)], 0x10000u) >> 16;
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int i = 8 * c + k;
+        const int i = 8 * g + k;
         if ((selm >> i) & 1u) {
-          // orderable key (-0 folded onto +0) into a fresh register: the
-          // 64-bit store takes an aligned pair, and a copy keeps the
-          // compiler from pinning all 32 items to pairs
+          // the key goes into a fresh register: the 64-bit store takes an
+          // aligned pair, and a copy keeps the compiler from pinning all 32
+          // items to pairs
           uint32_t kc;
           asm volatile("v_mov_b32 %0, %1" : "=v"(kc) : "v"(order_key(x[i])));
-          sm.x.comp[pos[k]] = ((uint64_t)kc << 32) | (uint32_t)(~(uint32_t)(p0 + i));
+          const uint32_t lo = (bin_of(i) << kPosBits) | (kPosMask - (uint32_t)pos_of(i));
+          sm.x.comp[slot[k]] = ((uint64_t)kc << 32) | lo;
         }
       }
     }
   }
   __syncthreads();
 
+  // G. order: rank inside the bin.  After the scatter a bin's packed word is
+  //    ((offset + count) << 16 | count).
   if (crowd <= (uint32_t)kCrowd) {
-    // rank inside the bin: after the scatter a bin's packed word is
-    // ((offset + count) << 16 | count).  The bin is scanned four entries per
-    // step with no branch in the step: four independent LDS reads (index
-    // clamped inside the list), then masked compares.
-    uint64_t it[kBItems];
-    uint32_t dst[kBItems];
+    uint64_t it[kBK / kBT];
+    uint32_t dst[kBK / kBT];
 #pragma unroll
-    for (int m = 0; m < kBItems; ++m) {
-      const int q = kBItems * t + m;
+    for (int m = 0; m < kBK / kBT; ++m) {
+      const int q = t + kBT * m;
       it[m] = 0ull;
       dst[m] = 0u;
       if (q < cnt) {
         it[m] = sm.x.comp[q];
-        const uint32_t w = sm.bins[bin(key_to_float((uint32_t)(it[m] >> 32)))];
+        const uint32_t w = sm.bins[((uint32_t)it[m] >> kPosBits) & (kBins - 1)];
         const uint32_t len = w & 0xFFFFu, s0 = (w >> 16) - len;
+        const uint64_t* e = &sm.x.comp[s0];
         uint32_t rk = 0u;
         for (uint32_t j = 0; j < len; j += 4) {
-          uint64_t v[4];
-#pragma unroll
-          for (uint32_t k = 0; k < 4; ++k) {
-            const uint32_t x2 = s0 + j + k;
-            v[k] = sm.x.comp[x2 < (uint32_t)kBK ? x2 : (uint32_t)kBK - 1u];
-          }
-#pragma unroll
-          for (uint32_t k = 0; k < 4; ++k)
-            rk += (uint32_t)(j + k < len) & (uint32_t)(v[k] > it[m]);
+          rk += (uint32_t)(e[j] > it[m]) + (uint32_t)(e[j + 1] > it[m]) +
+                (uint32_t)(e[j + 2] > it[m]) + (uint32_t)(e[j + 3] > it[m]);
         }
         dst[m] = s0 + rk;
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < kBItems; ++m)
-      if (kBItems * t + m < cnt) sm.x.comp[dst[m]] = it[m];
+    for (int m = 0; m < kBK / kBT; ++m)
+      if (t + kBT * m < cnt) sm.x.comp[dst[m]] = it[m];
     __syncthreads();
   } else {
     const int P = next_pow2(cnt);
@@ -449,12 +502,13 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
     bitonic_sort_desc<kBT>(sm.x.comp, P);
   }
 
-  // coalesced output of the ordered row, then the padding.  Positions are
-  // < n by construction; the clamp only keeps an id_map lookup in bounds.
+  // H. coalesced output of the ordered row, then the padding.  Positions
+  //    are < n by construction; the clamp only keeps an id_map lookup in
+  //    bounds.
   for (int q = t; q < K; q += kBT) {
     if (q < cnt) {
       const uint64_t c = sm.x.comp[q];
-      uint32_t p = ~(uint32_t)c;
+      uint32_t p = kPosMask - ((uint32_t)c & kPosMask);
       p = p < (uint32_t)n ? p : 0u;
       oi[q] = idmap ? idmap[p] : (int32_t)(start + p);
       if (os) os[q] = key_to_float((uint32_t)(c >> 32));
