@@ -44,6 +44,7 @@ constexpr int kBrute = 256;           // largest b1 ranked item by item
 constexpr int kCrowd = 64;            // largest per-bin count ranked by scanning the bin
 constexpr int kPosBits = 13;          // positions < kBN
 constexpr uint32_t kPosMask = (1u << kPosBits) - 1u;
+constexpr int kRowBufWord3 = 0x00020000;  // buffer resource word 3: raw 32-bit dword access
 
 struct alignas(16) BlockSmem {
   uint32_t bins[kBins];  // histogram, then packed (cursor << 16 | selected count)
@@ -154,53 +155,36 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
 
   // A. load.  A NaN score is taken as -inf (its order is unspecified; this
   //    makes every comparison below a total preorder on floats, -0 == +0).
-  for (int i = t; i < kBins; i += kBT) sm.bins[i] = 0u;
+  //    Every position is loaded through a buffer resource bounded at the
+  //    row's end, so the 32 loads go out unconditionally and a position past
+  //    the end reads 0.  Those zeros take part in the value range (which
+  //    then covers 0 as well: still a valid range, at worst a coarser one)
+  //    and the registers are never rewritten; only the bin counts and the
+  //    selection mask them out.
+#pragma unroll
+  for (int k = 0; k < kBins / (4 * kBT); ++k)
+    *reinterpret_cast<uint4*>(&sm.bins[4 * t + 4 * kBT * k]) = make_uint4(0u, 0u, 0u, 0u);
   if (t == 0) lcount = 0;
   auto clean = [](float v) { return v == v ? v : -__builtin_inff(); };
   float x[kBPer];
   {
-    const float* rp = row + base;
-    const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, n * 4, kRowBufWord3);
+    // each offset is made opaque so that no two loads are merged into a
+    // multi-dword access (whose bounds check need not be per dword)
 #pragma unroll
-    for (int j = 0; j < kBGroups; ++j) {
-      if (vec && j < gfull) {
-        const float4 q = *reinterpret_cast<const float4*>(rp + kBStep * j);
-        x[4 * j + 0] = q.x;
-        x[4 * j + 1] = q.y;
-        x[4 * j + 2] = q.z;
-        x[4 * j + 3] = q.w;
-      } else if (j < gused) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          x[4 * j + c] = ((vm >> (4 * j + c)) & 1u) ? rp[kBStep * j + c] : 0.0f;
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) x[4 * j + c] = 0.0f;
-      }
+    for (int i = 0; i < kBPer; ++i) {
+      int o = 4 * pos_of(i);
+      asm volatile("" : "+v"(o));
+      x[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0));
     }
   }
   float vlo = __builtin_inff(), vhi = -__builtin_inff();
 #pragma unroll
-  for (int j = 0; j < kBGroups; ++j) {
-    if (j < gfull) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float& v = x[4 * j + c];
-        v = clean(v);
-        vlo = __builtin_fminf(vlo, v);
-        vhi = __builtin_fmaxf(vhi, v);
-      }
-    } else if (j < gused) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float& v = x[4 * j + c];
-        v = clean(v);
-        if ((vm >> (4 * j + c)) & 1u) {
-          vlo = __builtin_fminf(vlo, v);
-          vhi = __builtin_fmaxf(vhi, v);
-        }
-      }
-    }
+  for (int i = 0; i < kBPer; ++i) {
+    x[i] = clean(x[i]);
+    vlo = __builtin_fminf(vlo, x[i]);
+    vhi = __builtin_fmaxf(vhi, x[i]);
   }
   {
     const uint32_t klo = __ockl_wfred_min_u32(order_key(vlo));
@@ -230,25 +214,13 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   const float scale0 = ((float)kBins - 0.01f) / span;
   const bool flat = !(span > 0.0f) || !(span <= 3.0e38f) || !(scale0 <= 3.0e38f);
   const float scale = flat ? 0.0f : scale0;
+  const uint32_t keep_bins = flat ? 0u : 0xFFFFFFFFu;
   // the bins are computed once and kept packed, two per register
-  // (positions past the row's end hold vmin, so every conversion is in range)
   uint32_t pk[kBPer / 2];
 #pragma unroll
-  for (int j = 0; j < kBGroups; ++j) {
-    if (j < gused && !flat) {
-      if (j >= gfull) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) x[4 * j + c] = ((vm >> (4 * j + c)) & 1u) ? x[4 * j + c] : vmin;
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        pk[2 * j + h] = (uint32_t)((x[4 * j + 2 * h] - vmin) * scale) |
-                        ((uint32_t)((x[4 * j + 2 * h + 1] - vmin) * scale) << 16);
-    } else {
-      pk[2 * j] = 0u;
-      pk[2 * j + 1] = 0u;
-    }
-  }
+  for (int j = 0; j < kBPer / 2; ++j)
+    pk[j] = ((uint32_t)((x[2 * j] - vmin) * scale) |
+             ((uint32_t)((x[2 * j + 1] - vmin) * scale) << 16)) & keep_bins;
   auto bin_of = [&](int i) -> uint32_t { return (pk[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu; };
 #pragma unroll
   for (int j = 0; j < kBGroups; ++j) {
