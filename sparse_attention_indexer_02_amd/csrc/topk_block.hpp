@@ -47,7 +47,8 @@ constexpr uint32_t kPosMask = (1u << kPosBits) - 1u;
 constexpr int kRowBufWord3 = 0x00020000;  // buffer resource word 3: raw 32-bit dword access
 
 struct alignas(16) BlockSmem {
-  uint32_t bins[kBins];  // histogram, then packed (cursor << 16 | selected count)
+  uint32_t bins[kBins + 64];  // histogram, then packed (cursor << 16 | selected count);
+                              // then one scratch word per lane
   union {
     uint64_t comp[kBK + 4];  // selected composites grouped by bin (+ 4 zero
                              // entries past the last), then the ordered row
@@ -165,7 +166,12 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   for (int k = 0; k < kBins / (4 * kBT); ++k)
     *reinterpret_cast<uint4*>(&sm.bins[4 * t + 4 * kBT * k]) = make_uint4(0u, 0u, 0u, 0u);
   if (t == 0) lcount = 0;
-  auto clean = [](float v) { return v == v ? v : -__builtin_inff(); };
+  // (adding +0 also turns -0 into +0, so the keys below need no fold)
+  auto clean = [](float v) { return v == v ? v + 0.0f : -__builtin_inff(); };
+  auto key_of = [](float v) {  // order_key for a value that is not -0
+    const uint32_t u = __float_as_uint(v);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+  };
   float x[kBPer];
   {
     const __amdgpu_buffer_rsrc_t rs =
@@ -300,19 +306,19 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   int n_gt = 0, n_eq = 0;
   if (select) {
     const int need = K - ab1;  // rank of T among b1's items, >= 1
-    uint32_t inb = 0u;         // which of this thread's items lie in b1
+    // which of this thread's items lie in b1 (masks are built by doubling
+    // and adding each compare, highest item first: one add per item)
+    uint32_t inb = 0u;
 #pragma unroll
-    for (int i = 0; i < kBPer; ++i) inb |= ((int)bin_of(i) == b1) ? (1u << i) : 0u;
+    for (int i = kBPer - 1; i >= 0; --i) inb = inb + inb + (uint32_t)((int)bin_of(i) == b1);
     inb &= vm;
     if (in_bin <= kBrute) {
-      // b1 holds few items: each position is a uniform skip unless some
-      // lane of the wave has one there (the mask is re-derived per position
-      // so the compiler does not hold 32 of them)
-#pragma unroll
-      for (int i = 0; i < kBPer; ++i) {
-        asm volatile("" : "+v"(inb));
-        if ((inb >> i) & 1u) sm.x.list[atomicAdd(&lcount, 1)] = __float_as_uint(x[i]);
-      }
+      // b1 holds few items: each holder walks its set bits, re-reading the
+      // score (a cached load, cleaned as in A) rather than indexing its
+      // registers
+      for (uint32_t mb = inb; mb != 0u; mb &= mb - 1u)
+        sm.x.list[atomicAdd(&lcount, 1)] =
+            __float_as_uint(clean(row[pos_of((int)__builtin_ctz(mb))]));
       __syncthreads();
       if (t < in_bin) {
         const float me = __uint_as_float(sm.x.list[t]);
@@ -370,15 +376,16 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   uint32_t selm = vm;
   if (select) {
     const int need_eq = K - n_gt;
-    uint32_t gtm = 0u, eqm = 0u;
+    uint32_t gem = 0u;
 #pragma unroll
-    for (int i = 0; i < kBPer; ++i) {
-      gtm |= x[i] > thr ? (1u << i) : 0u;
-      eqm |= x[i] == thr ? (1u << i) : 0u;
-    }
-    gtm &= vm;
-    eqm &= vm;
+    for (int i = kBPer - 1; i >= 0; --i) gem = gem + gem + (uint32_t)(x[i] >= thr);
+    selm = gem & vm;
     if (need_eq < n_eq) {  // uniform: T is tied past the K-th place
+      uint32_t eqm = 0u;
+#pragma unroll
+      for (int i = kBPer - 1; i >= 0; --i) eqm = eqm + eqm + (uint32_t)(x[i] == thr);
+      eqm &= vm;
+      const uint32_t gtm = selm & ~eqm;
       for (int i = t; i < kBN / 32; i += kBT) sm.x.eq.bits[i] = 0u;
       __syncthreads();
       // the four positions of group j share word (t >> 3) + 32 j
@@ -402,10 +409,9 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
           keep |= rank < need_eq ? (1u << i) : 0u;
         }
       }
-      eqm = keep;
+      selm = gtm | keep;
       __syncthreads();  // the bitmap area is reused by the scatter
     }
-    selm = gtm | eqm;
   }
 
   // F. scatter the selected items grouped by bin (cursor = packed high
@@ -415,12 +421,15 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
 #pragma unroll
   for (int g = 0; g < kBGroups / 2; ++g) {
     if (2 * g < gused) {
+      // (every item takes part, an unselected one on a word of its own lane
+      // past the bins: with no branch around them the eight atomics are all
+      // in flight before the first result is used)
       uint32_t slot[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int i = 8 * g + k;
-        slot[k] = 0u;
-        if ((selm >> i) & 1u) slot[k] = atomicAdd(&sm.bins[bin_of(i)], 0x10000u) >> 16;
+        const uint32_t b = ((selm >> i) & 1u) ? bin_of(i) : (uint32_t)(kBins + (t & 63));
+        slot[k] = atomicAdd(&sm.bins[b], 0x10000u);
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -430,9 +439,9 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
           // aligned pair, and a copy keeps the compiler from pinning all 32
           // items to pairs
           uint32_t kc;
-          asm volatile("v_mov_b32 %0, %1" : "=v"(kc) : "v"(order_key(x[i])));
+          asm volatile("v_mov_b32 %0, %1" : "=v"(kc) : "v"(key_of(x[i])));
           const uint32_t lo = (bin_of(i) << kPosBits) | (kPosMask - (uint32_t)pos_of(i));
-          sm.x.comp[slot[k]] = ((uint64_t)kc << 32) | lo;
+          sm.x.comp[slot[k] >> 16] = ((uint64_t)kc << 32) | lo;
         }
       }
     }
