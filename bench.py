@@ -27,8 +27,11 @@ sys.path.insert(0, ROOT)
 METRIC = "indexer query·key pairs scored+top-K'd /sec at H64 D128 K2048; % MFMA/HBM peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one non-packed fp32 op per lane-cycle
-PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# fp32 vector issue rate: the published 157.3 TFLOP/s counts an FMA as two
+# flops, i.e. 78.6 T fp32 lane-operations/s (256 CUs x 128 lanes x 2.4 GHz).
+# The block kernel issues its multiplies and adds as separate instructions,
+# each one lane-operation.
+PEAK_VALU_TOPS = 256 * 128 * 2.4e9 / 1e12
 
 
 def log(msg):
@@ -264,7 +267,7 @@ def bench_block(args):
                  roofline=dict(bound="alu", achieved=ach, peak=PEAK_VALU_TOPS, unit="TFLOP/s",
                                frac=ach / PEAK_VALU_TOPS,
                                traffic=counters_for("block"),
-                               kernel="block_max"))
+                               kernel="block_max128"))
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         n = 4

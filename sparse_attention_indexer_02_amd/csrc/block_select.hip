@@ -137,7 +137,14 @@ __global__ __launch_bounds__(kBlkThreads) void block_max(BlockArgs a) {
 // positions 4 (t % 32) .. +3 of the block: per d step three 16-byte LDS
 // reads feed 32 separately rounded products and 32 adds, in d order from +0
 // exactly as the scalar definition.  Block maxima: over the thread's 4
-// positions, then across the 32 lanes sharing the rows.
+// positions, then across the 32 lanes sharing the rows; lane j of those 32
+// keeps the maxima of the run's block j and the run's maxima leave as one
+// 128-byte row segment per row.
+// Workgroup order: workgroups go to the 8 XCDs round robin, so workgroup b
+// runs on XCD b % 8.  Each XCD takes every tile for one run after another
+// (runs x, 15 - x, 16 + x, 31 - x, ... for XCD x: equal causal work per
+// XCD), so the workgroups resident on an XCD share one run's keys (2 MB at
+// D 128) in its L2 and the keys come from HBM about once.
 // ---------------------------------------------------------------------------
 constexpr int kBmRows = 64;
 constexpr int kBmPos = 128;
@@ -145,13 +152,17 @@ constexpr int kBmDC = 16;
 constexpr int kBmMaxD = 128;
 constexpr int kBmRun = 32;  // blocks per workgroup
 
-__global__ __launch_bounds__(256) void block_max128(BlockArgs a, int runs) {
+__global__ __launch_bounds__(256) void block_max128(BlockArgs a, int runs, int64_t tiles) {
   __shared__ __attribute__((aligned(16))) float qs[kBmMaxD][kBmRows];
   __shared__ __attribute__((aligned(16))) float ks[2][kBmDC][kBmPos];
   __shared__ int64_t rpos[kBmRows];
   __shared__ int64_t tile_blocks;
   const int t = threadIdx.x;
-  const int tile = (int)(blockIdx.x / runs), run = (int)(blockIdx.x % runs);
+  const int xcd = (int)(blockIdx.x % 8);
+  const int64_t seq = blockIdx.x / 8;
+  const int64_t slot = seq / tiles, tile = seq % tiles;
+  const int run = (int)(8 * slot + ((slot & 1) ? 7 - xcd : xcd));
+  if (run >= runs) return;  // padding of the run count to a multiple of 8
   const int64_t nrows = (int64_t)a.n_q * a.H;
   const int64_t row0 = (int64_t)tile * kBmRows;
   const int D = a.D;
@@ -185,6 +196,10 @@ __global__ __launch_bounds__(256) void block_max128(BlockArgs a, int runs) {
   const int nchunk = (D + kBmDC - 1) / kBmDC;
   // key staging: thread t loads position t / 2, d's (t & 1) * 8 .. +7 of the chunk
   const int sp = t >> 1, sd = (t & 1) * 8;
+  // lane pg keeps the maxima of the run's block b_lo + pg for its 8 rows
+  float keep[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) keep[i] = -__builtin_inff();
   // fetch a chunk into registers before the compute, write it to LDS after
   float kr[8];
   auto fetch = [&](int64_t b, int c) {
@@ -250,10 +265,14 @@ __global__ __launch_bounds__(256) void block_max128(BlockArgs a, int runs) {
       }
 #pragma unroll
       for (int o = 16; o > 0; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o, 64));
-      const int64_t row = row0 + 8 * rg + i;
-      if (pg == 0 && row < nrows && b < mynb[i])
-        a.bscore[row * a.max_blocks + b] = m;
+      keep[i] = pg == (int)(b - b_lo) ? m : keep[i];
     }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = row0 + 8 * rg + i;
+    const int64_t b = b_lo + pg;
+    if (row < nrows && b < b_hi && b < mynb[i]) a.bscore[row * a.max_blocks + b] = keep[i];
   }
 }
 
@@ -349,7 +368,9 @@ hipError_t launch_block_select(const float* q, const float* k, const int64_t* qp
   if (bs == kBmPos && D <= kBmMaxD && a.max_blocks > 0) {
     const int64_t tiles = ((int64_t)n_q * H + kBmRows - 1) / kBmRows;
     const int runs = (int)((a.max_blocks + kBmRun - 1) / kBmRun);
-    hipLaunchKernelGGL(block_max128, dim3((unsigned)(tiles * runs)), dim3(256), 0, st, a, runs);
+    const int64_t runs8 = (runs + 7) / 8 * 8;
+    hipLaunchKernelGGL(block_max128, dim3((unsigned)(tiles * runs8)), dim3(256), 0, st, a, runs,
+                       tiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else {
