@@ -44,10 +44,13 @@ __global__ __launch_bounds__(256, 2) void score_mfma_shared(
 
 // ---------------------------------------------------------------------------
 // Per-row keys (decode layout), bf16 or fp8 keys.  Grid (rows, chunks); each
-// wave takes 32-key tiles of its row's chunk.  Lane l handles key l%32 and
-// the D-half l/32: in k-step s it supplies d = (D/2)(l/32) + 8 s + 0..7, so
-// each lane reads one contiguous half-row; the query fragments use the same
-// d order.
+// wave takes the 32-key tiles wave, wave + 4, ... of its row's chunk.  Lane l
+// handles key l%32 and the D-half l/32: in k-step s it supplies d =
+// (D/2)(l/32) + 8 s + 0..7, so each lane reads one contiguous half-row; the
+// query fragments use the same d order.  The keys go straight to registers
+// (no reuse across rows), one tile ahead of the MFMAs, through buffer
+// resources bounded at the chunk's end (loads past it read zero, stores past
+// it are dropped), so neither loads nor stores sit under a branch.
 // ---------------------------------------------------------------------------
 constexpr int kRowsChunk = 2048;  // keys per workgroup
 
@@ -58,13 +61,15 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows(
     const int32_t* __restrict__ vis_len, int n_q, int H, int64_t n_k, int64_t max_vis,
     float* __restrict__ scores, int64_t score_stride) {
   constexpr int D = 16 * KS;
+  constexpr int ES = FP8 ? 1 : 2;        // bytes per key element
+  constexpr int NL = FP8 ? KS / 2 : KS;  // 16-byte loads per lane per tile
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = blockIdx.x;
   int64_t off;
   const int64_t v = visible_len(vis_len, row_off, r, n_k, max_vis, &off);
   const int64_t c0 = (int64_t)blockIdx.y * kRowsChunk;
   if (c0 >= v) return;
-  const int64_t c1 = (c0 + kRowsChunk < v) ? c0 + kRowsChunk : v;
+  const int nk = (int)((c0 + kRowsChunk < v) ? kRowsChunk : v - c0);
 
   bf16x8 a[1][MT][KS];
   float wv[MT][16];
@@ -85,48 +90,65 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows(
     load_w_frag<MT>(w, w_stride, r, H, true, wv);
   }
 
-  for (int64_t t0 = c0 + (int64_t)wave * 32; t0 < c1; t0 += 4 * 32) {
-    const int64_t j = t0 + (lane & 31);
-    const bool in = j < c1;
-    const int64_t key = off + (in ? j : c0);
-    f32x16 acc[1][MT];
-    if (FP8) {
-      // D/2 fp8 bytes per lane = KS * 8 bytes.
-      const uint8_t* kb = reinterpret_cast<const uint8_t*>(kv) + key * D + (lane >> 5) * (D / 2);
-      uint32_t raw[2 * KS];
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const char*>(kv) + (off + c0) * D * ES), (short)0, nk * D * ES,
+      kBufWord3);
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(FP8 ? kscale + off + c0 : kscale), (short)0, FP8 ? nk * 4 : 0, kBufWord3);
+  const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(scores + (int64_t)r * score_stride + c0), (short)0, nk * 4, kBufWord3);
+  const int lk = lane & 31;
+  const int lane_off = lk * D * ES + (lane >> 5) * (D / 2) * ES;
+
+  auto load = [&](int tt, u32x4 (&raw)[NL], float& sc) {
+    const int o = tt * D * ES + lane_off;
 #pragma unroll
-      for (int c = 0; c < KS / 2; ++c) {
-        u32x4 x = in ? reinterpret_cast<const u32x4*>(kb)[c] : u32x4{0u, 0u, 0u, 0u};
-        raw[4 * c + 0] = x[0];
-        raw[4 * c + 1] = x[1];
-        raw[4 * c + 2] = x[2];
-        raw[4 * c + 3] = x[3];
-      }
-      mfma_tiles<1, MT, KS>(
-          a,
-          [&](int s) {
+    for (int c = 0; c < NL; ++c) raw[c] = __builtin_amdgcn_raw_buffer_load_b128(krs, o + 16 * c, 0, 0);
+    sc = FP8 ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(crs, (tt + lk) * 4, 0, 0))
+             : 1.0f;
+  };
+  auto compute = [&](int tt, const u32x4 (&raw)[NL], float sc) {
+    f32x16 acc[1][MT];
+    mfma_tiles<1, MT, KS>(
+        a,
+        [&](int s) {
+          if (FP8) {
             u32x4 bb;
 #pragma unroll
             for (int hw = 0; hw < 2; ++hw) {
-              uint32_t word = raw[2 * s + hw];
+              const uint32_t word = raw[s / 2][2 * (s % 2) + hw];
               auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false);
               auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true);
               bb[2 * hw + 0] = __builtin_bit_cast(uint32_t, p0);
               bb[2 * hw + 1] = __builtin_bit_cast(uint32_t, p1);
             }
             return as_bf16x8(bb);
-          },
-          acc);
-    } else {
-      const u32x4* kb = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(kv) +
-                                                       key * D + (lane >> 5) * (D / 2));
-      mfma_tiles<1, MT, KS>(
-          a, [&](int s) { return as_bf16x8(in ? kb[s] : u32x4{0u, 0u, 0u, 0u}); }, acc);
-    }
+          }
+          return as_bf16x8(raw[s]);
+        },
+        acc);
     float s = head_reduce<MT>(acc[0], wv);
-    if (FP8) s *= (in ? kscale[key] : 0.0f);
-    if (lane < 32 && in) scores[(int64_t)r * score_stride + j] = s;
+    if (FP8) s *= sc;
+    // lanes 32-63 hold the same sums; their out-of-range offset drops them
+    const int o = lane < 32 ? (tt + lane) * 4 : INT32_MAX;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s), ors, o, 0, 0);
+  };
+
+  // tiles wave * 32 + 128 i, i < n_i; two register sets alternate so the
+  // next tile's loads are in flight during each tile's MFMAs
+  const int first = wave * 32;
+  const int n_i = first < nk ? (nk - first + 127) / 128 : 0;
+  u32x4 ra[NL], rb[NL];
+  float sa = 0.0f, sb = 0.0f;
+  if (n_i > 0) load(first, ra, sa);
+  int i = 0;
+  for (; i + 1 < n_i; i += 2) {
+    load(first + 128 * (i + 1), rb, sb);
+    compute(first + 128 * i, ra, sa);
+    load(first + 128 * (i + 2), ra, sa);  // past the chunk: reads zero, never used
+    compute(first + 128 * (i + 1), rb, sb);
   }
+  if (i < n_i) compute(first + 128 * i, ra, sa);
 }
 
 // ---------------------------------------------------------------------------
