@@ -152,6 +152,152 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows(
 }
 
 // ---------------------------------------------------------------------------
+// Per-row fp8 keys (decode layout), staged through LDS by the buffer unit.
+// Same lane roles and arithmetic as score_mfma_rows<.., true>; each wave owns
+// a ring of kRingTiles tile buffers in LDS that the buffer loads fill
+// directly (no registers held for the prefetch), kRingTiles - 1 tiles ahead
+// of the MFMAs, so several tiles per wave are in flight.  A tile's 16-byte
+// chunks are placed at slot k * CPK + (c ^ (k % CPK)) (key k, chunk c), so
+// the MFMA-order reads (8 lanes = 8 keys, same chunk) hit distinct banks;
+// the loader lanes cover 8 whole keys per instruction.  The key scales ride
+// along (one dword per key).  A wave only ever reads its own ring, so the
+// waits are the wave's own load counter, no barrier.  Loads past the chunk
+// are clamped to its last key.
+// ---------------------------------------------------------------------------
+constexpr int kRingTiles = 3;
+
+// LDS byte address of a shared-memory object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// One buffer-unit load straight into LDS: 16 (or 4) bytes per lane from the
+// lane's global address into lds + 16 (or 4) * lane.  Written as assembly so
+// that the compiler's own wait placement does not treat every later LDS
+// read as depending on it; the kernel waits on the load counter itself.
+__device__ __forceinline__ void lds_load16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
+template <int MT, int KS>
+__global__ __launch_bounds__(256, 2) void score_mfma_rows_fp8(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
+    const float* __restrict__ kscale, const float* __restrict__ w, int64_t w_stride,
+    const int64_t* __restrict__ row_off, const int32_t* __restrict__ vis_len, int n_q, int H,
+    int64_t n_k, int64_t max_vis, float* __restrict__ scores, int64_t score_stride) {
+  constexpr int D = 16 * KS;
+  constexpr int CPK = D / 16;      // 16-byte chunks per key
+  constexpr int TB = 32 * D;       // bytes per 32-key tile
+  constexpr int NDMA = TB / 1024;  // 64-lane x 16-byte loads per tile
+  constexpr int NB = kRingTiles;
+  __shared__ __attribute__((aligned(16))) unsigned char kbuf[4][NB][TB];
+  __shared__ __attribute__((aligned(16))) float sbuf[4][NB][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = blockIdx.x;
+  int64_t off;
+  const int64_t v = visible_len(vis_len, row_off, r, n_k, max_vis, &off);
+  const int64_t c0 = (int64_t)blockIdx.y * kRowsChunk;
+  if (c0 >= v) return;
+  const int nk = (int)((c0 + kRowsChunk < v) ? kRowsChunk : v - c0);
+
+  bf16x8 a[1][MT][KS];
+  float wv[MT][16];
+  {
+    const int hf = lane >> 5;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      int h = mt * 32 + (lane & 31);
+      bool ok = h < H;
+      const u32x4* src =
+          reinterpret_cast<const u32x4*>(q + ((int64_t)r * H + (ok ? h : 0)) * D + hf * (D / 2));
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        u32x4 x = ok ? src[s] : u32x4{0u, 0u, 0u, 0u};
+        a[0][mt][s] = as_bf16x8(x);
+      }
+    }
+    load_w_frag<MT>(w, w_stride, r, H, true, wv);
+  }
+  const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(scores + (int64_t)r * score_stride + c0), (short)0, nk * 4, kBufWord3);
+
+  const int first = wave * 32;
+  const int n_i = first < nk ? (nk - first + 127) / 128 : 0;
+  // this lane's share of a tile load: slot p = 64 d + lane holds key p / CPK,
+  // chunk (p % CPK) ^ (key % CPK)
+  int gkey[NDMA], gch[NDMA];
+#pragma unroll
+  for (int d = 0; d < NDMA; ++d) {
+    const int p = 64 * d + lane;
+    gkey[d] = p / CPK;
+    gch[d] = (p % CPK) ^ (gkey[d] % CPK);
+  }
+  const uint8_t* kc = kv + (off + c0) * D;
+  const float* sc0 = kscale + off + c0;
+  // ring tile i of this wave = keys first + 128 i ..; a key past the chunk
+  // is read as the chunk's last key (its score is never stored)
+  const uint32_t kring = __builtin_amdgcn_readfirstlane(lds_addr(&kbuf[wave][0][0]));
+  const uint32_t sring = __builtin_amdgcn_readfirstlane(lds_addr(&sbuf[wave][0][0]));
+  auto issue = [&](int i) {
+    const int tt = first + 128 * i, b = i % NB;
+#pragma unroll
+    for (int d = 0; d < NDMA; ++d) {
+      const int key = tt + gkey[d] < nk ? tt + gkey[d] : nk - 1;
+      lds_load16(kc + (int64_t)key * D + gch[d] * 16, kring + b * TB + 1024 * d);
+    }
+    const int key = tt + lane < nk ? tt + lane : nk - 1;
+    lds_load4(sc0 + key, sring + b * 256);
+  };
+  const int lk = lane & 31, hf = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < NB - 1; ++i) issue(i);
+  for (int i = 0; i < n_i; ++i) {
+    // the buffer refilled here was read in step i - 1, whose reads have
+    // been consumed
+    __builtin_amdgcn_sched_barrier(0);
+    issue(i + NB - 1);
+    // tile i's loads are complete once at most the later tiles' loads
+    // (issued after it, and returned in order) are outstanding
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NB - 1) * (NDMA + 1)) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned char* tb = &kbuf[wave][i % NB][0];
+    u32x4 ch[CPK / 2];
+#pragma unroll
+    for (int j = 0; j < CPK / 2; ++j) {
+      const int c = hf * (CPK / 2) + j;
+      ch[j] = *reinterpret_cast<const u32x4*>(tb + 16 * (lk * CPK + (c ^ (lk % CPK))));
+    }
+    const float sc = sbuf[wave][i % NB][lk];
+    f32x16 acc[1][MT];
+    mfma_tiles<1, MT, KS>(
+        a,
+        [&](int s) {
+          u32x4 bb;
+#pragma unroll
+          for (int hw = 0; hw < 2; ++hw) {
+            const uint32_t word = ch[s / 2][2 * (s % 2) + hw];
+            auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false);
+            auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true);
+            bb[2 * hw + 0] = __builtin_bit_cast(uint32_t, p0);
+            bb[2 * hw + 1] = __builtin_bit_cast(uint32_t, p1);
+          }
+          return as_bf16x8(bb);
+        },
+        acc);
+    float s = head_reduce<MT>(acc[0], wv) * sc;
+    // lanes 32-63 hold the same sums; their out-of-range offset drops them
+    const int o = lane < 32 ? (first + 128 * i + lane) * 4 : INT32_MAX;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s), ors, o, 0, 0);
+  }
+  // no load may still be writing this wave's ring when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
 // Generic VALU path: one thread per (row, key), fp32 arithmetic.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float decode_elem(const void* p, si_dtype dt, int64_t i) {
@@ -232,10 +378,11 @@ static hipError_t launch_mfma(const ScoreArgs& a, const int32_t* row_list,
     const int64_t chunks = (a.max_vis + kRowsChunk - 1) / kRowsChunk;
     dim3 grid((unsigned)a.n_q, (unsigned)(chunks > 0 ? chunks : 1));
     if (a.k_dtype == SI_FP8_E4M3FN)
-      hipLaunchKernelGGL((score_mfma_rows<MT, KS, true>), grid, dim3(256), 0, st,
-                         reinterpret_cast<const uint16_t*>(a.q), a.k, a.k_scale, a.w,
-                         a.w_row_stride, a.k_row_offset, a.vis_len, a.n_q, a.H, a.n_k, a.max_vis,
-                         a.scores, a.score_stride);
+      hipLaunchKernelGGL((score_mfma_rows_fp8<MT, KS>), grid, dim3(256), 0, st,
+                         reinterpret_cast<const uint16_t*>(a.q),
+                         reinterpret_cast<const uint8_t*>(a.k), a.k_scale, a.w, a.w_row_stride,
+                         a.k_row_offset, a.vis_len, a.n_q, a.H, a.n_k, a.max_vis, a.scores,
+                         a.score_stride);
     else
       hipLaunchKernelGGL((score_mfma_rows<MT, KS, false>), grid, dim3(256), 0, st,
                          reinterpret_cast<const uint16_t*>(a.q), a.k, a.k_scale, a.w,
