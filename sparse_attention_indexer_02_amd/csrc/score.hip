@@ -157,9 +157,11 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows(
 // a ring of kRingTiles tile buffers in LDS that the buffer loads fill
 // directly (no registers held for the prefetch), kRingTiles - 1 tiles ahead
 // of the MFMAs, so several tiles per wave are in flight.  A tile's 16-byte
-// chunks are placed at slot k * CPK + (c ^ (k % CPK)) (key k, chunk c), so
-// the MFMA-order reads (8 lanes = 8 keys, same chunk) hit distinct banks;
-// the loader lanes cover 8 whole keys per instruction.  The key scales ride
+// chunks are placed at slot k * CPK + (c ^ f(k)) (key k, chunk c, f(k) =
+// (k % 8) ^ ((k / 8) % 2), taken mod CPK), so the MFMA-order reads (lanes =
+// keys, same chunk) of 8 or 16 consecutive keys hit distinct 16-byte bank
+// groups whether one LDS cycle serves 128 or 256 bytes; the loader lanes
+// cover 8 whole keys per instruction.  The key scales ride
 // along (one dword per key).  A wave only ever reads its own ring, so the
 // waits are the wave's own load counter, no barrier.  Loads past the chunk
 // are clamped to its last key.
@@ -204,6 +206,37 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows_fp8(
   if (c0 >= v) return;
   const int nk = (int)((c0 + kRowsChunk < v) ? kRowsChunk : v - c0);
 
+  const int first = wave * 32;
+  const int n_i = first < nk ? (nk - first + 127) / 128 : 0;
+  // this lane's share of a tile load: slot p = 64 d + lane holds key p / CPK,
+  // chunk (p % CPK) ^ (key % CPK)
+  auto swz = [](int k) { return ((k & 7) ^ ((k >> 3) & 1)) % CPK; };
+  int gkey[NDMA], gch[NDMA];
+#pragma unroll
+  for (int d = 0; d < NDMA; ++d) {
+    const int p = 64 * d + lane;
+    gkey[d] = p / CPK;
+    gch[d] = (p % CPK) ^ swz(gkey[d]);
+  }
+  const uint8_t* kc = kv + (off + c0) * D;
+  const float* sc0 = kscale + off + c0;
+  // ring tile i of this wave = keys first + 128 i ..; a key past the chunk
+  // is read as the chunk's last key (its score is never stored)
+  const uint32_t kring = __builtin_amdgcn_readfirstlane(lds_addr(&kbuf[wave][0][0]));
+  const uint32_t sring = __builtin_amdgcn_readfirstlane(lds_addr(&sbuf[wave][0][0]));
+  auto issue = [&](int i) {
+    const int tt = first + 128 * i, b = i % NB;
+#pragma unroll
+    for (int d = 0; d < NDMA; ++d) {
+      const int key = tt + gkey[d] < nk ? tt + gkey[d] : nk - 1;
+      lds_load16(kc + (int64_t)key * D + gch[d] * 16, kring + b * TB + 1024 * d);
+    }
+    const int key = tt + lane < nk ? tt + lane : nk - 1;
+    lds_load4(sc0 + key, sring + b * 256);
+  };
+  const int lk = lane & 31, hf = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < NB - 1; ++i) issue(i);
   bf16x8 a[1][MT][KS];
   float wv[MT][16];
   {
@@ -225,36 +258,6 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows_fp8(
   const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(scores + (int64_t)r * score_stride + c0), (short)0, nk * 4, kBufWord3);
 
-  const int first = wave * 32;
-  const int n_i = first < nk ? (nk - first + 127) / 128 : 0;
-  // this lane's share of a tile load: slot p = 64 d + lane holds key p / CPK,
-  // chunk (p % CPK) ^ (key % CPK)
-  int gkey[NDMA], gch[NDMA];
-#pragma unroll
-  for (int d = 0; d < NDMA; ++d) {
-    const int p = 64 * d + lane;
-    gkey[d] = p / CPK;
-    gch[d] = (p % CPK) ^ (gkey[d] % CPK);
-  }
-  const uint8_t* kc = kv + (off + c0) * D;
-  const float* sc0 = kscale + off + c0;
-  // ring tile i of this wave = keys first + 128 i ..; a key past the chunk
-  // is read as the chunk's last key (its score is never stored)
-  const uint32_t kring = __builtin_amdgcn_readfirstlane(lds_addr(&kbuf[wave][0][0]));
-  const uint32_t sring = __builtin_amdgcn_readfirstlane(lds_addr(&sbuf[wave][0][0]));
-  auto issue = [&](int i) {
-    const int tt = first + 128 * i, b = i % NB;
-#pragma unroll
-    for (int d = 0; d < NDMA; ++d) {
-      const int key = tt + gkey[d] < nk ? tt + gkey[d] : nk - 1;
-      lds_load16(kc + (int64_t)key * D + gch[d] * 16, kring + b * TB + 1024 * d);
-    }
-    const int key = tt + lane < nk ? tt + lane : nk - 1;
-    lds_load4(sc0 + key, sring + b * 256);
-  };
-  const int lk = lane & 31, hf = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < NB - 1; ++i) issue(i);
   for (int i = 0; i < n_i; ++i) {
     // the buffer refilled here was read in step i - 1, whose reads have
     // been consumed
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows_fp8(
 #pragma unroll
     for (int j = 0; j < CPK / 2; ++j) {
       const int c = hf * (CPK / 2) + j;
-      ch[j] = *reinterpret_cast<const u32x4*>(tb + 16 * (lk * CPK + (c ^ (lk % CPK))));
+      ch[j] = *reinterpret_cast<const u32x4*>(tb + 16 * (lk * CPK + (c ^ swz(lk))));
     }
     const float sc = sbuf[wave][i % NB][lk];
     f32x16 acc[1][MT];
