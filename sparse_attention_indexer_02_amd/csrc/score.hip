@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma_shared(
 // resources bounded at the chunk's end (loads past it read zero, stores past
 // it are dropped), so neither loads nor stores sit under a branch.
 // ---------------------------------------------------------------------------
-constexpr int kRowsChunk = 2048;  // keys per workgroup
+constexpr int kRowsChunk = 4096;  // keys per workgroup
 
 template <int MT, int KS, bool FP8>
 __global__ __launch_bounds__(256, 2) void score_mfma_rows(
