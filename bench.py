@@ -196,7 +196,7 @@ def bench_indexer(args, cfg, workload):
         ach = score_bytes / st["score"] / 1e6
         roof = dict(bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=ach / PEAK_HBM_GBS, traffic=counters_for(workload),
-                    kernel="score_mfma_rows")
+                    kernel="score_mfma_rows_fp8")
     else:
         # the score kernel: MFMA work over its own (stage) time
         ach = kern["score_stage"]["tflops"]
