@@ -5,14 +5,14 @@
 
 Default workload: the DSA-style causal prefill chunk, 8192 queries x 8192
 keys, H=64, D=128, bf16, K=2048, then the segment-witness merge (S=16,
-serving keep/budget).  One step = score rows (MFMA kernel) -> top-K ids
-(radix-select kernel) -> witness merge, all on the current HIP stream with
-inputs resident in HBM.  value = visible query-key pairs per second of the
-whole step.  Per-kernel times come from HIP events recorded on that stream
-around each stage.
+serving keep/budget).  One step = idx_score_topk (score rows with the MFMA
+kernel, then the block top-K) -> witness merge, all on the current HIP stream
+with inputs resident in HBM.  value = visible query-key pairs per second of
+the whole step.  Per-kernel times come from HIP events recorded on that
+stream around each stage.
 
-Prints ONE JSON line.  With --gpus N > 1 it exits: this build measures one
-GPU (row sharding across GPUs is described in the design notes).
+Prints ONE JSON line.  With --gpus N > 1 it exits: it measures one GPU (row
+sharding across GPUs is described in the design notes).
 """
 import argparse
 import hashlib
