@@ -35,17 +35,11 @@ __device__ __forceinline__ float relu(float x) {
 __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Score epilogue: s = sum_h w_h max(x_h, 0) for this lane's key column.
-// Fixed order: the fma chain runs over e = mt * 16 + v in increasing e, then
-// lanes 0-31's partial is added to lanes 32-63's.  The order is part of what
-// makes a score the same bits everywhere; head_chain lets a caller split the
-// chain into pieces (interleaved with other work) without changing it.
-template <int MT>
-__device__ __forceinline__ void head_chain(const f32x16 (&acc)[MT], const float (&wv)[MT][16],
-                                           int e0, int e1, float& s) {
-#pragma unroll
-  for (int e = e0; e < e1; ++e) s = __builtin_fmaf(wv[e / 16][e % 16], relu(acc[e / 16][e % 16]), s);
-}
-
+// Fixed order: one fma chain per head tile mt over v = 0..15 in increasing
+// v (two independent chains keep the VALU busy with MT = 2), the tiles'
+// partials added in increasing mt, then lanes 0-31's partial is added to
+// lanes 32-63's.  The order is part of what makes a score the same bits
+// everywhere: every path that produces a (query, key) score calls this.
 __device__ __forceinline__ float halves_sum(float s) {
   float o = __shfl_xor(s, 32, 64);
   return (threadIdx.x & 32) ? o + s : s + o;
@@ -53,8 +47,16 @@ __device__ __forceinline__ float halves_sum(float s) {
 
 template <int MT>
 __device__ __forceinline__ float head_reduce(const f32x16 (&acc)[MT], const float (&wv)[MT][16]) {
-  float s = 0.0f;
-  head_chain<MT>(acc, wv, 0, 16 * MT, s);
+  float p[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    p[mt] = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) p[mt] = __builtin_fmaf(wv[mt][v], relu(acc[mt][v]), p[mt]);
+  }
+  float s = p[0];
+#pragma unroll
+  for (int mt = 1; mt < MT; ++mt) s += p[mt];
   return halves_sum(s);
 }
 
