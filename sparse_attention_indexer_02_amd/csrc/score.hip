@@ -20,26 +20,45 @@
 namespace si {
 
 // ---------------------------------------------------------------------------
-// Shared-key prefill kernel: one workgroup per 4 QPW rows, longest first.
+// Shared-key prefill kernel: one workgroup per 4 QPW rows and key segment.
+// With one segment (keys that fit an XCD's L2) the groups run longest
+// first.  With several, workgroup b runs on XCD b % 8 (round-robin
+// dispatch) and the XCDs walk the segments in step: each takes an eighth of
+// the groups (longest first) for segment 0, then for segment 1, ..., so the
+// workgroups resident on an XCD share one segment's keys in its L2 and the
+// keys come from HBM about once per XCD.
 // ---------------------------------------------------------------------------
+constexpr int64_t kSegBytes = 1 << 20;        // shared keys per segment
+constexpr int64_t kSegThreshold = 2 << 20;    // keys bytes beyond which to segment
+
 template <int MT, int KS, int QPW>
 __global__ __launch_bounds__(256, 2) void score_mfma_shared(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     int64_t w_stride, const int32_t* __restrict__ vis_len, int n_q, int H, int64_t n_k,
     int64_t max_vis, float* __restrict__ scores, int64_t score_stride,
-    const int32_t* __restrict__ row_list, const int32_t* __restrict__ row_count) {
+    const int32_t* __restrict__ row_list, const int32_t* __restrict__ row_count, int nseg,
+    int64_t seg_keys) {
   constexpr int QB = 4 * QPW;
   __shared__ __attribute__((aligned(16))) unsigned char lds[score_lds_bytes<KS>()];
-  int n_act = n_q;
-  int g = (int)blockIdx.x;
-  if (row_list) {
-    n_act = *row_count;
-    if (g * QB >= n_act) return;
+  const int n_act = row_list ? *row_count : n_q;
+  const int G = (n_q + QB - 1) / QB;  // groups the grid was sized for
+  int g;
+  int64_t key_lo = 0, key_hi = max_vis;
+  if (nseg <= 1) {
+    g = (int)blockIdx.x;
+    if (!row_list) g = G - 1 - g;  // longest rows (highest index) first
   } else {
-    g = (n_q + QB - 1) / QB - 1 - g;  // longest rows (highest index) first
+    const int G8 = (G + 7) / 8;  // groups per XCD per segment
+    const int xcd = (int)(blockIdx.x % 8), seq = (int)(blockIdx.x / 8);
+    const int seg = seq / G8, gi = xcd + 8 * (seq % G8);
+    if (gi >= G) return;
+    g = row_list ? gi : G - 1 - gi;
+    key_lo = (int64_t)seg * seg_keys;
+    key_hi = key_lo + seg_keys;
   }
+  if (g * QB >= n_act) return;
   score_group_shared<MT, KS, QPW>(q, k, w, w_stride, vis_len, H, n_k, max_vis, scores,
-                                  score_stride, row_list, n_act, g, lds);
+                                  score_stride, row_list, n_act, g, key_lo, key_hi, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -372,11 +391,16 @@ static hipError_t launch_mfma(const ScoreArgs& a, const int32_t* row_list,
   if (shared) {
     constexpr int QPW = (MT == 1) ? 2 : 1;
     const int groups = (a.n_q + 4 * QPW - 1) / (4 * QPW);
-    hipLaunchKernelGGL((score_mfma_shared<MT, KS, QPW>), dim3(groups), dim3(256), 0, st,
+    const int64_t vis_keys = a.max_vis < a.n_k ? a.max_vis : a.n_k;
+    const int64_t seg_keys = kSegBytes / (a.D * 2);
+    const int nseg =
+        vis_keys * a.D * 2 > kSegThreshold ? (int)((vis_keys + seg_keys - 1) / seg_keys) : 1;
+    const int64_t grid = nseg > 1 ? (int64_t)(groups + 7) / 8 * 8 * nseg : groups;
+    hipLaunchKernelGGL((score_mfma_shared<MT, KS, QPW>), dim3((unsigned)grid), dim3(256), 0, st,
                        reinterpret_cast<const uint16_t*>(a.q),
                        reinterpret_cast<const uint16_t*>(a.k), a.w, a.w_row_stride, a.vis_len,
                        a.n_q, a.H, a.n_k, a.max_vis, a.scores, a.score_stride, row_list,
-                       row_count);
+                       row_count, nseg, seg_keys);
   } else {
     const int64_t chunks = (a.max_vis + kRowsChunk - 1) / kRowsChunk;
     dim3 grid((unsigned)a.n_q, (unsigned)(chunks > 0 ? chunks : 1));

@@ -18,8 +18,9 @@ constexpr int score_lds_bytes() {
 }
 
 // Scores of the rows in slots g * 4 QPW .. of the workgroup (slot s -> row
-// row_list ? row_list[s] : s, slots >= n_act empty), one wave per QPW of
-// them: heads on the MFMA rows (32x32x16 bf16), keys on the columns, D the
+// row_list ? row_list[s] : s, slots >= n_act empty) for the keys [key_lo,
+// key_hi) (key_lo a multiple of 32), one wave per QPW of them: heads on the
+// MFMA rows (32x32x16 bf16), keys on the columns, D the
 // reduction; 32-key tiles of the shared keys are staged through LDS
 // (double buffered) and read from L2 once per workgroup for all its rows;
 // the ReLU * w head sum runs on the accumulator tile in registers.  lds is
@@ -30,7 +31,7 @@ __device__ __forceinline__ void score_group_shared(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     int64_t w_stride, const int32_t* __restrict__ vis_len, int H, int64_t n_k, int64_t max_vis,
     float* __restrict__ scores, int64_t score_stride, const int32_t* __restrict__ row_list,
-    int n_act, int g, unsigned char* lds_base) {
+    int n_act, int g, int64_t key_lo, int64_t key_hi, unsigned char* lds_base) {
   constexpr int D = 16 * KS;
   constexpr int QB = 4 * QPW;                  // queries per workgroup
   constexpr int ROWB = D * 2 + 16;             // padded LDS row: conflict-free b128 reads
@@ -48,7 +49,7 @@ __device__ __forceinline__ void score_group_shared(
 
   int myrow[QPW];
   int64_t vis[QPW];
-  int64_t end = 0;
+  int64_t end = 0;  // keys any row of the group sees
   for (int i = 0; i < QB; ++i) {
     int r = row_of(i);
     int64_t off, v = 0;
@@ -59,7 +60,8 @@ __device__ __forceinline__ void score_group_shared(
       myrow[i % QPW] = r;
     }
   }
-  if (end == 0) return;
+  end = end < key_hi ? end : key_hi;
+  if (end <= key_lo) return;
 
   bf16x8 a[QPW][MT][KS];
   float wv[QPW][MT][16];
@@ -69,7 +71,7 @@ __device__ __forceinline__ void score_group_shared(
     load_w_frag<MT>(w, w_stride, myrow[i], H, myrow[i] >= 0, wv[i]);
   }
 
-  const int ntiles = (int)((end + 31) / 32);
+  const int t_lo = (int)(key_lo / 32), ntiles = (int)((end + 31) / 32);
   u32x4 pre[CPT];
   static_assert(CHUNKS % 256 == 0, "every thread stages whole chunks");
   // Keys and score rows go through buffer resources: 32-bit offsets (one
@@ -102,11 +104,11 @@ __device__ __forceinline__ void score_group_shared(
   };
   const unsigned char* lrow = &lds[0][(lane & 31) * ROWB + (lane >> 5) * 16];
 
-  fetch(0);
-  stash(0);
+  fetch(t_lo);
+  stash(t_lo & 1);
   wait_memory();
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = t_lo; t < ntiles; ++t) {
     fetch(t + 1 < ntiles ? t + 1 : t);  // the last one is a harmless repeat
     __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
     const unsigned char* brow = lrow + (t & 1) * (32 * ROWB);
