@@ -43,6 +43,13 @@ def test_prefill_small(orc, n_q, L, H, D, K):
     _all_rows(orc, synth.prefill(seed=n_q, n_q=n_q, L=L, H=H, D=D, topk=K))
 
 
+@pytest.mark.parametrize("n_q,L,H,D,K", [(96, 12500, 32, 128, 512), (48, 20000, 64, 64, 1024)])
+def test_prefill_key_segments(orc, n_q, L, H, D, K):
+    """Shared keys beyond 2 MiB are scored in 1 MiB key segments (4 and 3
+    segments here, the last one ragged); every row against the oracle."""
+    _all_rows(orc, synth.prefill(seed=L, n_q=n_q, L=L, H=H, D=D, topk=K))
+
+
 def test_shared_weights(orc):
     cfg = synth.prefill(seed=5, n_q=128, L=400, H=64, D=128, topk=100)
     cfg["w"] = np.ascontiguousarray(cfg["w"][0])
