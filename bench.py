@@ -370,8 +370,8 @@ def bench_dosa(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "decode", "dosa", "dosa_structured", "block"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
