@@ -518,13 +518,14 @@ __global__ void dosa_knorm(const uint16_t* k, int64_t n_k, int D, float* knorm) 
 
 // Bound scan: MFMA over the 32-row plan tile of QPW rows per wave, shared
 // key tiles through LDS; writes one 32-bit survivor mask per (row, tile).
+// One workgroup per 4 QPW rows and key segment (score_micro.hpp).
 template <int KS, int QPW>
 __global__ __launch_bounds__(256, 2) void dosa_bound(
     const DosaCtx* ctx, const uint16_t* __restrict__ plan_a, const float* __restrict__ plan_w,
     const float* __restrict__ plan_c, const float* __restrict__ top_score, int topk,
     const uint16_t* __restrict__ k, const float* __restrict__ knorm,
     const uint32_t* __restrict__ seed_mask, const int32_t* __restrict__ vis_len, int n_q,
-    int64_t n_k, uint32_t* __restrict__ bitmap, int64_t words) {
+    int64_t n_k, uint32_t* __restrict__ bitmap, int64_t words, int nseg, int64_t seg_keys) {
   constexpr int D = 16 * KS;
   constexpr int QB = 4 * QPW;
   constexpr int ROWB = D * 2 + 16;
@@ -534,7 +535,9 @@ __global__ __launch_bounds__(256, 2) void dosa_bound(
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][32 * ROWB];
   if (ctx->global_fallback) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = (n_q + QB - 1) / QB - 1 - (int)blockIdx.x;
+  int g;
+  int64_t key_lo, key_hi;
+  if (!segment_of((n_q + QB - 1) / QB, nseg, seg_keys, n_k, true, &g, &key_lo, &key_hi)) return;
   const int r0 = g * QB;
   int64_t vis[QPW];
   float tau[QPW], cr[QPW];
@@ -550,7 +553,8 @@ __global__ __launch_bounds__(256, 2) void dosa_bound(
       cr[i % QPW] = r < n_q ? plan_c[r] : 0.0f;
     }
   }
-  if (end == 0) return;
+  end = end < key_hi ? end : key_hi;
+  if (end <= key_lo) return;
   bf16x8 a[QPW][1][KS];
   float wv[QPW][1][16];
 #pragma unroll
@@ -559,7 +563,7 @@ __global__ __launch_bounds__(256, 2) void dosa_bound(
     load_q_frag<1, KS>(plan_a, r, 32, r < n_q, a[i]);
     load_w_frag<1>(plan_w, 32, r, 32, r < n_q, wv[i]);
   }
-  const int ntiles = (int)((end + 31) / 32);
+  const int t_lo = (int)(key_lo / 32), ntiles = (int)((end + 31) / 32);
   u32x4 pre[CPT];
   auto fetch = [&](int t) {
 #pragma unroll
@@ -580,10 +584,10 @@ __global__ __launch_bounds__(256, 2) void dosa_bound(
       if (ch < CHUNKS) *reinterpret_cast<u32x4*>(&lds[buf][key * ROWB + part * 16]) = pre[c];
     }
   };
-  fetch(0);
-  stash(0);
+  fetch(t_lo);
+  stash(t_lo & 1);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = t_lo; t < ntiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < ntiles) fetch(t + 1);
     const unsigned char* brow = &lds[buf][(lane & 31) * ROWB + (lane >> 5) * 16];
@@ -841,10 +845,14 @@ static hipError_t run_dosa(const uint16_t* q, const uint16_t* k, const float* w,
           p->kept_heads, p->neg_active_frac, I(L.stat_cnt), F(L.stat_sum), U16(L.plan_a),
           F(L.plan_w), F(L.plan_c)));
   SI_TRY((dosa_knorm, dim3(grid_for(n_k, 256)), dim3(256), 0, st, k, n_k, D, F(L.knorm)));
-  SI_TRY(((dosa_bound<KS, 2>), dim3((n_q + 7) / 8), dim3(256), 0, st, ctx, U16(L.plan_a),
-          F(L.plan_w), F(L.plan_c), F(L.top_score), topk, k, F(L.knorm),
-          reinterpret_cast<const uint32_t*>(ws + L.seed_mask), vis, n_q, n_k,
-          reinterpret_cast<uint32_t*>(ws + L.bitmap), words));
+  {
+    int64_t seg_keys;
+    const int nseg = key_segments(n_k, D, &seg_keys);
+    SI_TRY(((dosa_bound<KS, 2>), dim3((unsigned)segment_grid((n_q + 7) / 8, nseg)), dim3(256), 0,
+            st, ctx, U16(L.plan_a), F(L.plan_w), F(L.plan_c), F(L.top_score), topk, k,
+            F(L.knorm), reinterpret_cast<const uint32_t*>(ws + L.seed_mask), vis, n_q, n_k,
+            reinterpret_cast<uint32_t*>(ws + L.bitmap), words, nseg, seg_keys));
+  }
   SI_TRY((dosa_compact, dim3(n_q), dim3(kCompThreads), 0, st, ctx,
           reinterpret_cast<const uint32_t*>(ws + L.bitmap), words, vis, n_k, cap, I(L.surv_ids),
           I(L.surv_cnt), I(L.row_fb)));

@@ -20,17 +20,9 @@
 namespace si {
 
 // ---------------------------------------------------------------------------
-// Shared-key prefill kernel: one workgroup per 4 QPW rows and key segment.
-// With one segment (keys that fit an XCD's L2) the groups run longest
-// first.  With several, workgroup b runs on XCD b % 8 (round-robin
-// dispatch) and the XCDs walk the segments in step: each takes an eighth of
-// the groups (longest first) for segment 0, then for segment 1, ..., so the
-// workgroups resident on an XCD share one segment's keys in its L2 and the
-// keys come from HBM about once per XCD.
+// Shared-key prefill kernel: one workgroup per 4 QPW rows and key segment
+// (segments as in score_micro.hpp; one segment when the keys fit an L2).
 // ---------------------------------------------------------------------------
-constexpr int64_t kSegBytes = 1 << 20;        // shared keys per segment
-constexpr int64_t kSegThreshold = 2 << 20;    // keys bytes beyond which to segment
-
 template <int MT, int KS, int QPW>
 __global__ __launch_bounds__(256, 2) void score_mfma_shared(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
@@ -43,19 +35,9 @@ __global__ __launch_bounds__(256, 2) void score_mfma_shared(
   const int n_act = row_list ? *row_count : n_q;
   const int G = (n_q + QB - 1) / QB;  // groups the grid was sized for
   int g;
-  int64_t key_lo = 0, key_hi = max_vis;
-  if (nseg <= 1) {
-    g = (int)blockIdx.x;
-    if (!row_list) g = G - 1 - g;  // longest rows (highest index) first
-  } else {
-    const int G8 = (G + 7) / 8;  // groups per XCD per segment
-    const int xcd = (int)(blockIdx.x % 8), seq = (int)(blockIdx.x / 8);
-    const int seg = seq / G8, gi = xcd + 8 * (seq % G8);
-    if (gi >= G) return;
-    g = row_list ? gi : G - 1 - gi;
-    key_lo = (int64_t)seg * seg_keys;
-    key_hi = key_lo + seg_keys;
-  }
+  int64_t key_lo, key_hi;
+  // listed rows keep list order; otherwise longest rows (highest index) first
+  if (!segment_of(G, nseg, seg_keys, max_vis, row_list == nullptr, &g, &key_lo, &key_hi)) return;
   if (g * QB >= n_act) return;
   score_group_shared<MT, KS, QPW>(q, k, w, w_stride, vis_len, H, n_k, max_vis, scores,
                                   score_stride, row_list, n_act, g, key_lo, key_hi, lds);
@@ -391,11 +373,9 @@ static hipError_t launch_mfma(const ScoreArgs& a, const int32_t* row_list,
   if (shared) {
     constexpr int QPW = (MT == 1) ? 2 : 1;
     const int groups = (a.n_q + 4 * QPW - 1) / (4 * QPW);
-    const int64_t vis_keys = a.max_vis < a.n_k ? a.max_vis : a.n_k;
-    const int64_t seg_keys = kSegBytes / (a.D * 2);
-    const int nseg =
-        vis_keys * a.D * 2 > kSegThreshold ? (int)((vis_keys + seg_keys - 1) / seg_keys) : 1;
-    const int64_t grid = nseg > 1 ? (int64_t)(groups + 7) / 8 * 8 * nseg : groups;
+    int64_t seg_keys;
+    const int nseg = key_segments(a.max_vis < a.n_k ? a.max_vis : a.n_k, a.D, &seg_keys);
+    const int64_t grid = segment_grid(groups, nseg);
     hipLaunchKernelGGL((score_mfma_shared<MT, KS, QPW>), dim3((unsigned)grid), dim3(256), 0, st,
                        reinterpret_cast<const uint16_t*>(a.q),
                        reinterpret_cast<const uint16_t*>(a.k), a.w, a.w_row_stride, a.vis_len,

@@ -118,4 +118,46 @@ __device__ __forceinline__ void mfma_tiles(const bf16x8 (&a)[QPW][MT][KS], BFrag
   }
 }
 
+// ---------------------------------------------------------------------------
+// Key segments for the kernels that stream keys shared by all rows.  Keys
+// beyond kSegThreshold bytes do not stay in one XCD's L2 while every resident
+// workgroup streams all of them, so the launch is cut into 1 MiB key
+// segments: workgroup b runs on XCD b % 8 (round-robin dispatch), and the
+// XCDs walk the segments in step, each taking an eighth of the row groups
+// (longest first unless the rows come from a list) for segment 0, then for
+// segment 1, ..., so the workgroups resident on an XCD share one segment.
+// ---------------------------------------------------------------------------
+constexpr int64_t kSegBytes = 1 << 20;
+constexpr int64_t kSegThreshold = 2 << 20;
+
+// Segment count and keys per segment for `keys` shared keys of D bf16.
+inline int key_segments(int64_t keys, int D, int64_t* seg_keys) {
+  *seg_keys = kSegBytes / ((int64_t)D * 2);
+  if (keys * D * 2 <= kSegThreshold) return 1;
+  return (int)((keys + *seg_keys - 1) / *seg_keys);
+}
+// Workgroups to launch for G row groups.
+inline int64_t segment_grid(int G, int nseg) {
+  return nseg > 1 ? (int64_t)(G + 7) / 8 * 8 * nseg : G;
+}
+// This workgroup's row group and key range; false for a padding workgroup.
+__device__ __forceinline__ bool segment_of(int G, int nseg, int64_t seg_keys, int64_t all_keys,
+                                           bool longest_first, int* g, int64_t* lo,
+                                           int64_t* hi) {
+  if (nseg <= 1) {
+    *g = longest_first ? G - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    *lo = 0;
+    *hi = all_keys;
+    return true;
+  }
+  const int G8 = (G + 7) / 8;  // groups per XCD per segment
+  const int xcd = (int)(blockIdx.x % 8), seq = (int)(blockIdx.x / 8);
+  const int seg = seq / G8, gi = xcd + 8 * (seq % G8);
+  if (gi >= G) return false;
+  *g = longest_first ? G - 1 - gi : gi;
+  *lo = (int64_t)seg * seg_keys;
+  *hi = *lo + seg_keys;
+  return true;
+}
+
 }  // namespace si
