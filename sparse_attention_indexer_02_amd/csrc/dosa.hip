@@ -584,20 +584,34 @@ __global__ __launch_bounds__(256, 2) void dosa_bound(
       if (ch < CHUNKS) *reinterpret_cast<u32x4*>(&lds[buf][key * ROWB + part * 16]) = pre[c];
     }
   };
+  // a key's norm and seed bit travel one tile ahead of its use, with the
+  // key tile itself
+  auto side = [&](int t, float& kn, uint32_t& sw) {
+    const int64_t j = (int64_t)t * 32 + (lane & 31);
+    kn = j < n_k ? knorm[j] : 0.0f;
+    sw = j < n_k ? seed_mask[j >> 5] : 0u;
+  };
+  float kn_n;
+  uint32_t sw_n;
   fetch(t_lo);
+  side(t_lo, kn_n, sw_n);
   stash(t_lo & 1);
   __syncthreads();
   for (int t = t_lo; t < ntiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) fetch(t + 1);
+    const float kn = kn_n;
+    const uint32_t sw = sw_n;
+    if (t + 1 < ntiles) {
+      fetch(t + 1);
+      side(t + 1, kn_n, sw_n);
+    }
     const unsigned char* brow = &lds[buf][(lane & 31) * ROWB + (lane >> 5) * 16];
     f32x16 acc[QPW][1];
     mfma_tiles<QPW, 1, KS>(
         a, [&](int s) { return as_bf16x8(*reinterpret_cast<const u32x4*>(brow + 32 * s)); },
         acc);
     const int64_t j = (int64_t)t * 32 + (lane & 31);
-    const float kn = j < n_k ? knorm[j] : 0.0f;
-    const bool seed = j < n_k && ((seed_mask[j >> 5] >> (j & 31)) & 1u);
+    const bool seed = (sw >> (j & 31)) & 1u;
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
       float u = head_reduce<1>(acc[i], wv[i]) + cr[i] * kn;
