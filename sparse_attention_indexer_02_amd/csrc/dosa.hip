@@ -382,22 +382,28 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
   return (uint16_t)(pick >> 16);
 }
 
-// Per-row plan (fp64).  One workgroup per row.
+// Per-row plan (fp64).  One workgroup per row.  q_h rows sit in LDS as
+// floats (bf16 values are exact there) with a padded stride, so per-head
+// loops over d hit distinct banks; every dot product and sum is taken in
+// fp64 in increasing index order.
 constexpr int kPlanThreads = 256;
+constexpr int kPlanStride = 128 + 1;  // floats per q_h row in LDS
 __global__ __launch_bounds__(kPlanThreads) void dosa_plan(
     const DosaCtx* ctx, const uint16_t* __restrict__ q, const float* __restrict__ w,
     int64_t w_stride, int H, int D, int n_seeds, int kept_heads, float neg_frac,
     const int32_t* __restrict__ stat_cnt, const float* __restrict__ stat_sum,
     uint16_t* __restrict__ plan_a, float* __restrict__ plan_w, float* __restrict__ plan_c) {
-  __shared__ double qd[64 * 128];
-  __shared__ double qq[64], wf[64], dn[64], beta[64], agg[128];
+  __shared__ float qf[64 * kPlanStride];
+  __shared__ double gdot[64][32];  // q_h . q_j for omitted h, kept index t
+  __shared__ double qq[64], wf[64], dn[64], beta[64], agg[128], part[2][128];
   __shared__ float imp[64];
   __shared__ int role[64], anchor[64], kept_list[32];
   __shared__ int n_kept;
   if (ctx->global_fallback) return;
   const int r = blockIdx.x, tid = threadIdx.x;
+  auto qv = [&](int h, int d) { return (double)qf[h * kPlanStride + d]; };
   for (int e = tid; e < H * D; e += kPlanThreads)
-    qd[e] = (double)__uint_as_float((uint32_t)q[(int64_t)r * H * D + e] << 16);
+    qf[(e / D) * kPlanStride + e % D] = __uint_as_float((uint32_t)q[(int64_t)r * H * D + e] << 16);
   for (int h = tid; h < H; h += kPlanThreads)
     imp[h] = fabsf(w[(int64_t)r * w_stride + h]) * (stat_sum[(int64_t)r * H + h] / (float)n_seeds);
   __syncthreads();
@@ -406,7 +412,7 @@ __global__ __launch_bounds__(kPlanThreads) void dosa_plan(
     for (int g = 0; g < H; ++g)
       rank += (imp[g] > imp[h] || (imp[g] == imp[h] && g < h)) ? 1 : 0;
     double s = 0.0;
-    for (int d = 0; d < D; ++d) s += qd[h * D + d] * qd[h * D + d];
+    for (int d = 0; d < D; ++d) s += qv(h, d) * qv(h, d);
     qq[h] = s;
     const float wh = w[(int64_t)r * w_stride + h];
     const float act = (float)stat_cnt[(int64_t)r * H + h] / (float)n_seeds;
@@ -421,6 +427,18 @@ __global__ __launch_bounds__(kPlanThreads) void dosa_plan(
   }
   __syncthreads();
   const int nk = n_kept;
+  // dot products of omitted positive heads with every kept head, one
+  // (head, kept) pair per thread
+  for (int e = tid; e < H * nk; e += kPlanThreads) {
+    const int h = e / nk, t = e % nk;
+    if (role[h] == 2) {
+      const int j = kept_list[t];
+      double g = 0.0;
+      for (int d = 0; d < D; ++d) g += qv(h, d) * qv(j, d);
+      gdot[h][t] = g;
+    }
+  }
+  __syncthreads();
   // anchors of omitted positive heads: smallest residual, lower head on ties
   if (tid < H) {
     int h = tid;
@@ -432,8 +450,7 @@ __global__ __launch_bounds__(kPlanThreads) void dosa_plan(
       int bj = -1;
       for (int t = 0; t < nk; ++t) {
         int j = kept_list[t];
-        double g = 0.0;
-        for (int d = 0; d < D; ++d) g += qd[h * D + d] * qd[j * D + d];
+        double g = gdot[h][t];
         double b = qq[j] > 0.0 ? g / qq[j] : 0.0;
         b = b < 0.0 ? 0.0 : b;
         double r2 = qq[h] - 2.0 * b * g + b * b * qq[j];
@@ -445,7 +462,7 @@ __global__ __launch_bounds__(kPlanThreads) void dosa_plan(
       }
       double s = 0.0;  // explicit |q_h - beta q_a|: no cancellation in the bound
       for (int d = 0; d < D; ++d) {
-        double e = qd[h * D + d] - (bj >= 0 ? bb * qd[bj * D + d] : 0.0);
+        double e = qv(h, d) - (bj >= 0 ? bb * qv(bj, d) : 0.0);
         s += e * e;
       }
       anchor[h] = bj;
@@ -467,8 +484,12 @@ __global__ __launch_bounds__(kPlanThreads) void dosa_plan(
   for (int d = tid; d < D; d += kPlanThreads) {
     double s = 0.0;
     for (int h = 0; h < H; ++h)
-      if (role[h] == 3) s += fabs((double)w[(int64_t)r * w_stride + h]) * qd[h * D + d];
+      if (role[h] == 3) s += fabs((double)w[(int64_t)r * w_stride + h]) * qv(h, d);
     agg[d] = s;
+    // the aggregate's bf16 carrier and its rounding error, per d
+    const double ah = (double)__uint_as_float((uint32_t)f64_to_bf16_rne(s) << 16);
+    part[0][d] = (s - ah) * (s - ah);
+    part[1][d] = ah * ah;
   }
   __syncthreads();
   uint16_t* pa = plan_a + (int64_t)r * 32 * D;
@@ -494,9 +515,8 @@ __global__ __launch_bounds__(kPlanThreads) void dosa_plan(
       if (role[h] == 1) nwf += fabs(wf[h]) * sqrt(qq[h]);
     }
     for (int d = 0; d < D; ++d) {
-      double ah = (double)__uint_as_float((uint32_t)f64_to_bf16_rne(agg[d]) << 16);
-      err2 += (agg[d] - ah) * (agg[d] - ah);
-      ah2 += ah * ah;
+      err2 += part[0][d];
+      ah2 += part[1][d];
     }
     double err = sqrt(err2), ahn = sqrt(ah2);
     double C = R + err + 0x1p-10 * (nw + nwf + ahn + R + err);
