@@ -584,47 +584,52 @@ __global__ __launch_bounds__(256, 2) void dosa_bound(
     load_w_frag<1>(plan_w, 32, r, 32, r < n_q, wv[i]);
   }
   const int t_lo = (int)(key_lo / 32), ntiles = (int)((end + 31) / 32);
+  static_assert(CHUNKS % 256 == 0, "every thread stages whole chunks");
+  // keys, norms and seed words through buffer resources (zero past n_k, no
+  // branch around a load; n_k * D * 2 < 2^31 is checked by the caller)
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)k, (short)0, (int)(n_k * D * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t nrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)knorm, (short)0, (int)(n_k * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)seed_mask, (short)0, (int)(((n_k + 31) / 32) * 4), 0x00020000);
   u32x4 pre[CPT];
   auto fetch = [&](int t) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      int ch = threadIdx.x + 256 * c;
-      int key = ch / CPK, part = ch % CPK;
-      int64_t j = (int64_t)t * 32 + key;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ch < CHUNKS && j < n_k) v = reinterpret_cast<const u32x4*>(k + j * D)[part];
-      pre[c] = v;
-    }
+    for (int c = 0; c < CPT; ++c)
+      pre[c] = __builtin_amdgcn_raw_buffer_load_b128(
+          krs, t * (32 * D * 2) + ((int)threadIdx.x + 256 * c) * 16, 0, 0);
   };
   auto stash = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       int ch = threadIdx.x + 256 * c;
       int key = ch / CPK, part = ch % CPK;
-      if (ch < CHUNKS) *reinterpret_cast<u32x4*>(&lds[buf][key * ROWB + part * 16]) = pre[c];
+      *reinterpret_cast<u32x4*>(&lds[buf][key * ROWB + part * 16]) = pre[c];
     }
   };
-  // a key's norm and seed bit travel one tile ahead of its use, with the
+  // a key's norm and seed word travel one tile ahead of their use, with the
   // key tile itself
   auto side = [&](int t, float& kn, uint32_t& sw) {
-    const int64_t j = (int64_t)t * 32 + (lane & 31);
-    kn = j < n_k ? knorm[j] : 0.0f;
-    sw = j < n_k ? seed_mask[j >> 5] : 0u;
+    kn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                       nrs, (t * 32 + (lane & 31)) * 4, 0, 0));
+    sw = __builtin_amdgcn_raw_buffer_load_b32(mrs, t * 4, 0, 0);
   };
   float kn_n;
   uint32_t sw_n;
   fetch(t_lo);
   side(t_lo, kn_n, sw_n);
   stash(t_lo & 1);
+  wait_memory();
   __syncthreads();
   for (int t = t_lo; t < ntiles; ++t) {
     const int buf = t & 1;
     const float kn = kn_n;
     const uint32_t sw = sw_n;
-    if (t + 1 < ntiles) {
-      fetch(t + 1);
-      side(t + 1, kn_n, sw_n);
-    }
+    const int tn = t + 1 < ntiles ? t + 1 : t;  // the last one is a harmless repeat
+    fetch(tn);
+    side(tn, kn_n, sw_n);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the MFMAs
     const unsigned char* brow = &lds[buf][(lane & 31) * ROWB + (lane >> 5) * 16];
     f32x16 acc[QPW][1];
     mfma_tiles<QPW, 1, KS>(
@@ -641,7 +646,8 @@ __global__ __launch_bounds__(256, 2) void dosa_bound(
       if (lane == 0 && r < n_q && (int64_t)t * 32 < vis[i])
         bitmap[(int64_t)r * words + t] = (uint32_t)m;
     }
-    if (t + 1 < ntiles) stash(buf ^ 1);
+    // buffer buf ^ 1 held tile t - 1, read before the previous barrier
+    stash(buf ^ 1);
     __syncthreads();
   }
 }
