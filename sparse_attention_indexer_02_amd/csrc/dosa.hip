@@ -293,32 +293,34 @@ __global__ __launch_bounds__(256, 2) void dosa_seed_score(
       }
   }
   const int ntiles = (n_seeds + 31) / 32;
+  static_assert(CHUNKS % 256 == 0, "every thread stages whole chunks");
+  // seed keys through a buffer resource (zero past n_seeds, no branch
+  // around a load)
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)sk, (short)0, n_seeds * D * 2, 0x00020000);
   u32x4 pre[CPT];
   auto fetch = [&](int t) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      int ch = threadIdx.x + 256 * c;
-      int key = ch / CPK, part = ch % CPK;
-      int j = t * 32 + key;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ch < CHUNKS && j < n_seeds) v = reinterpret_cast<const u32x4*>(sk + (int64_t)j * D)[part];
-      pre[c] = v;
-    }
+    for (int c = 0; c < CPT; ++c)
+      pre[c] = __builtin_amdgcn_raw_buffer_load_b128(
+          krs, t * (32 * D * 2) + ((int)threadIdx.x + 256 * c) * 16, 0, 0);
   };
   auto stash = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       int ch = threadIdx.x + 256 * c;
       int key = ch / CPK, part = ch % CPK;
-      if (ch < CHUNKS) *reinterpret_cast<u32x4*>(&lds[buf][key * ROWB + part * 16]) = pre[c];
+      *reinterpret_cast<u32x4*>(&lds[buf][key * ROWB + part * 16]) = pre[c];
     }
   };
   fetch(0);
   stash(0);
+  wait_memory();
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) fetch(t + 1);
+    fetch(t + 1 < ntiles ? t + 1 : t);  // the last one is a harmless repeat
+    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
     const unsigned char* brow = &lds[buf][(lane & 31) * ROWB + (lane >> 5) * 16];
     f32x16 acc[QPW][MT];
     mfma_tiles<QPW, MT, KS>(
@@ -328,19 +330,21 @@ __global__ __launch_bounds__(256, 2) void dosa_seed_score(
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
       float s = head_reduce<MT>(acc[i], wv[i]);
-      // padding keys are zero: x = 0 adds nothing to either statistic
+      // padding keys are zero: x = 0 adds nothing to either statistic (the
+      // ReLU is the one the head sum took)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          float x = acc[i][mt][v];
+          const float x = relu(acc[i][mt][v]);
           cnt[i][mt][v] += x > 0.0f ? 1 : 0;
-          rs[i][mt][v] += __builtin_fmaxf(x, 0.0f);
+          rs[i][mt][v] += x;
         }
       if (lane < 32 && r0 + i < n_q && j < n_seeds)
         seed_scores[(int64_t)(r0 + i) * n_seeds + j] = s;
     }
-    if (t + 1 < ntiles) stash(buf ^ 1);
+    // buffer buf ^ 1 held tile t - 1, read before the previous barrier
+    stash(buf ^ 1);
     __syncthreads();
   }
   // reduce the statistics over the 32 key lanes of each half-wave
