@@ -200,17 +200,26 @@ __global__ __launch_bounds__(1024) void dosa_select_seeds(DosaCtx* ctx, const in
     if (threadIdx.x == 0 && bad) ctx->global_fallback = 1;
     return;
   }
-  for (int v = threadIdx.x; v <= R + 1; v += T) ge[v] = 0;
+  // per-wave histograms of the counts (atomics contend within a wave only),
+  // then ge[v] := #{count >= v}
+  __shared__ int hw[T / 64][kMaxRep + 2];
+  const int wv = threadIdx.x >> 6;
+  for (int v = threadIdx.x & 63; v <= R + 1; v += 64) hw[wv][v] = 0;
   __syncthreads();
   for (int j = threadIdx.x; j < c; j += T) {
     int cnt = counts[j];
     cnt = cnt > R ? R : cnt;
-    atomicAdd(&ge[cnt], 1);
+    atomicAdd(&hw[wv][cnt], 1);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {  // ge[v] := #{count >= v}
-    for (int v = R - 1; v >= 0; --v) ge[v] += ge[v + 1];
+  for (int v = threadIdx.x; v <= R + 1; v += T) {
+    int sum = 0;
+    for (int w2 = 0; w2 < T / 64; ++w2) sum += hw[w2][v];
+    ge[v] = sum;
   }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int v = R - 1; v >= 0; --v) ge[v] += ge[v + 1];
   __syncthreads();
   int vstar = 0;
   for (int v = R; v >= 0; --v)
@@ -219,22 +228,30 @@ __global__ __launch_bounds__(1024) void dosa_select_seeds(DosaCtx* ctx, const in
       break;
     }
   const int need_eq = n_seeds - ge[vstar + 1];  // taken among count == vstar, by key
-  int eq_before = 0, pos_before = 0;
-  for (int base = 0; base < c; base += T) {
-    int j = base + threadIdx.x;
-    int cnt = j < c ? (counts[j] > R ? R : counts[j]) : -1;
-    int is_eq = (cnt == vstar) ? 1 : 0;
-    int tot_eq;
-    int eq_rank = eq_before + block_excl_scan<T>(is_eq, red, &tot_eq);
-    int sel = (j < c) && (cnt > vstar || (is_eq && eq_rank < need_eq)) ? 1 : 0;
-    int tot_sel;
-    int pos = pos_before + block_excl_scan<T>(sel, red, &tot_sel);
-    if (sel) {
-      seeds[pos] = j;
+  // thread t owns the keys [t per, (t + 1) per): one scan of its count == vstar
+  // keys gives their index-order ranks, one scan of its selected keys their
+  // output slots (the seed list is in increasing key order)
+  const int per = (c + T - 1) / T;
+  const int j0 = (int)threadIdx.x * per, j1 = j0 + per < c ? j0 + per : c;
+  auto cnt_of = [&](int j) { return counts[j] > R ? R : counts[j]; };
+  int n_eq = 0;
+  for (int j = j0; j < j1; ++j) n_eq += cnt_of(j) == vstar ? 1 : 0;
+  int tot;
+  const int eq_base = block_excl_scan<T>(n_eq, red, &tot);
+  int n_sel = 0;
+  for (int j = j0, er = eq_base; j < j1; ++j) {
+    const int v = cnt_of(j);
+    n_sel += (v > vstar || (v == vstar && er < need_eq)) ? 1 : 0;
+    er += v == vstar ? 1 : 0;
+  }
+  int pos = block_excl_scan<T>(n_sel, red, &tot);
+  for (int j = j0, er = eq_base; j < j1; ++j) {
+    const int v = cnt_of(j);
+    if (v > vstar || (v == vstar && er < need_eq)) {
+      seeds[pos++] = j;
       atomicOr(&seed_mask[j >> 5], 1u << (j & 31));
     }
-    eq_before += tot_eq;
-    pos_before += tot_sel;
+    er += v == vstar ? 1 : 0;
   }
 }
 
