@@ -2,14 +2,18 @@
 // (DoSA reading notes, section 1: one consistent total order makes tied ids
 // reproducible; the final selection is by full score).
 //
-// Two kernels:
+// Kernels:
 //  * topk_block: rows of at most 8192 scores, K <= 2048, one workgroup per
-//    row holding the row in registers (see the kernel for the steps).
-//  * topk_rows: any length and K <= 4096 (long decode rows, DoSA's seed and
-//    fallback rows).  One 512-thread workgroup per row; rows up to 8192
-//    scores are staged in LDS, longer ones re-read per pass; a 3-pass radix
-//    select (11/11/10-bit digits) finds the K-th key, ties at it are taken in
-//    index order, and a bitonic sort of (key, ~index) composites orders them.
+//    row holding the row in registers (steps in topk_block.hpp).  Longer
+//    rows (K <= 2048, with a workspace) are cut into 8192-score chunks whose
+//    ordered top-K lists, with the chunks' position maps, are selected from
+//    again by the same kernel until one chunk remains (topk_next_len gives
+//    each level's row lengths).
+//  * topk_rows: K > 2048, or a long row without a workspace.  One
+//    512-thread workgroup per row; rows up to 8192 scores are staged in LDS,
+//    longer ones re-read per pass; a 3-pass radix select (11/11/10-bit
+//    digits) finds the K-th key, ties at it are taken in index order, and a
+//    bitonic sort of (key, ~index) composites orders them.
 #include "topk_block.hpp"
 
 namespace si {
