@@ -4,6 +4,8 @@
  *
  * Operations, each defined by the page cited at its declaration:
  *   idx_score_topk       lightning-indexer score + per-query top-K
+ *   idx_score_topk_prior the same result on the decode path, selecting only
+ *                        among keys above a threshold from recent keys
  *   dosa_prune_topk      the same top-K through DoSA's certified prune
  *   kvwitness_merge      segment-witness covering merge, in place
  *   block_sparse_select  MiniMax-M3 block-sparse block selection
@@ -104,6 +106,41 @@ si_status idx_score_topk(const void* q, si_dtype q_dtype, const void* k, si_dtyp
                          int32_t* out_idx, float* out_score, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 size_t idx_score_topk_workspace(int32_t n_q, int32_t H, int32_t D, int64_t max_vis, int32_t topk);
+
+/* ------------------------------------------------------------------------ *
+ * idx_score_topk_prior
+ *
+ * The decoding path of the DoSA reading notes, section 1: full FP8 (or bf16)
+ * scoring is kept, and a threshold built from recently selected keys cuts
+ * the score writeback and the selection work.  The threshold follows the
+ * notes' section 2 step 1: tau_r is the K-th largest score among at least K
+ * distinct visible keys, here the distinct ids of prior_ids row r in
+ * [0, vis_r), scored with every head; with fewer than K of them, tau_r is
+ * -inf.  Since those are K keys of the row, the row's K-th largest score is
+ * >= tau_r, and only keys with s >= tau_r are written and selected from.
+ *
+ * Arguments, layout and outputs as idx_score_topk, plus:
+ *  prior_ids  [n_q, prior_width] i32, row-relative ids (e.g. the previous
+ *          step's out_idx); entries outside [0, vis_r) and repeats are
+ *          ignored.  1 <= prior_width <= SI_MAX_PRIOR_WIDTH.
+ *  out_tau    [n_q] f32 or NULL: tau_r.
+ *  out_survivors [n_q] i32 or NULL: keys with s >= tau_r.
+ *  workspace  idx_score_topk_prior_workspace(n_q, max_vis, topk) bytes,
+ *          256-byte aligned.
+ * out_idx / out_score equal idx_score_topk's bit for bit whatever the prior.
+ * Supported: per-row keys (k_row_offset non-NULL), bf16 queries, bf16 or
+ * fp8 keys, H <= 64, D 64 or 128; other shapes or dtypes ->
+ * UNSUPPORTED_DTYPE.  Other errors as idx_score_topk.
+ * ------------------------------------------------------------------------ */
+#define SI_MAX_PRIOR_WIDTH 2048
+si_status idx_score_topk_prior(const void* q, si_dtype q_dtype, const void* k, si_dtype k_dtype,
+                               const float* k_scale, const float* w, int64_t w_row_stride,
+                               const int64_t* k_row_offset, const int32_t* vis_len, int32_t n_q,
+                               int32_t H, int32_t D, int64_t n_k, int64_t max_vis, int32_t topk,
+                               const int32_t* prior_ids, int32_t prior_width, int32_t* out_idx,
+                               float* out_score, float* out_tau, int32_t* out_survivors,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+size_t idx_score_topk_prior_workspace(int32_t n_q, int64_t max_vis, int32_t topk);
 
 /* The two stages of idx_score_topk, for callers that keep the score rows
  * (the notes' section 5 names score writeback and the selection input as

@@ -4,7 +4,9 @@ The computation lives in libsparse_indexer.so (hand-written HIP, C ABI in
 include/sparse_indexer.h); this package only marshals torch tensors into it.
 """
 from ._binding import (SparseIndexerError, block_sparse_select, dosa_prune_topk, idx_score,
-                       idx_score_topk, kvwitness_merge, lib, rows_topk, status_string)
+                       idx_score_topk, idx_score_topk_prior, kvwitness_merge, lib, rows_topk,
+                       status_string)
 
-__all__ = ["idx_score_topk", "idx_score", "rows_topk", "dosa_prune_topk", "kvwitness_merge",
-           "block_sparse_select", "SparseIndexerError", "lib", "status_string"]
+__all__ = ["idx_score_topk", "idx_score_topk_prior", "idx_score", "rows_topk",
+           "dosa_prune_topk", "kvwitness_merge", "block_sparse_select", "SparseIndexerError",
+           "lib", "status_string"]

@@ -44,6 +44,9 @@ SIGNATURES = {
     "idx_score_topk": (i32, [vp, i32, vp, i32, vp, vp, i64, vp, vp, i32, i32, i32, i64, i64, i32,
                              vp, vp, vp, sz, vp]),
     "idx_score_topk_workspace": (sz, [i32, i32, i32, i64, i32]),
+    "idx_score_topk_prior": (i32, [vp, i32, vp, i32, vp, vp, i64, vp, vp, i32, i32, i32, i64, i64,
+                                   i32, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
+    "idx_score_topk_prior_workspace": (sz, [i32, i64, i32]),
     "idx_score": (i32, [vp, i32, vp, i32, vp, vp, i64, vp, vp, i32, i32, i32, i64, i64, vp, i64,
                         vp]),
     "rows_topk": (i32, [vp, i64, vp, vp, i64, i64, i32, i32, vp, vp, vp, sz, vp]),
@@ -155,6 +158,44 @@ def idx_score_topk(q, k, w, vis_len, topk, *, k_scale=None, k_row_offset=None, m
                               _ptr(out_score), _ptr(ws), ws_bytes, _stream(dev))
     _check(st, "idx_score_topk")
     return out_idx, out_score
+
+
+def idx_score_topk_prior(q, k, w, vis_len, topk, prior_ids, *, k_scale=None, k_row_offset=None,
+                         max_vis=None, out_idx=None, out_score=None, want_scores=True,
+                         want_stats=False, workspace=None):
+    """idx_score_topk's result through the decode path that selects only among
+    keys at or above a threshold from the prior ids [n_q, P] (i32, e.g. the
+    previous step's ids).  Returns (idx, scores|None, stats|None) with stats =
+    (tau [n_q] f32, survivors [n_q] i32)."""
+    _dev_tensor(q, "q")
+    _dev_tensor(k, "k")
+    _dev_tensor(w, "w", torch.float32)
+    _dev_tensor(vis_len, "vis_len", torch.int32)
+    _dev_tensor(prior_ids, "prior_ids", torch.int32)
+    dev = q.device
+    n_q, H, D = q.shape
+    n_k = k.shape[0]
+    if max_vis is None:
+        max_vis = n_k if k_row_offset is None else (int(vis_len.max().item()) if n_q else 0)
+    w_stride = H if w.dim() == 2 else 0
+    if out_idx is None:
+        out_idx = torch.empty((n_q, topk), dtype=torch.int32, device=dev)
+    if out_score is None and want_scores:
+        out_score = torch.empty((n_q, topk), dtype=torch.float32, device=dev)
+    tau = surv = None
+    if want_stats:
+        tau = torch.empty(n_q, dtype=torch.float32, device=dev)
+        surv = torch.empty(n_q, dtype=torch.int32, device=dev)
+    need = lib().idx_score_topk_prior_workspace(n_q, max_vis, topk)
+    ws, ws_bytes = _workspace(need, dev, workspace)
+    st = lib().idx_score_topk_prior(_ptr(q), _dtype_code(q, "q"), _ptr(k), _dtype_code(k, "k"),
+                                    _ptr(k_scale), _ptr(w), w_stride, _ptr(k_row_offset),
+                                    _ptr(vis_len), n_q, H, D, n_k, max_vis, topk,
+                                    _ptr(prior_ids), prior_ids.shape[1], _ptr(out_idx),
+                                    _ptr(out_score), _ptr(tau), _ptr(surv), _ptr(ws), ws_bytes,
+                                    _stream(dev))
+    _check(st, "idx_score_topk_prior")
+    return out_idx, out_score, ((tau, surv) if want_stats else None)
 
 
 def idx_score(q, k, w, vis_len, *, k_scale=None, k_row_offset=None, max_vis=None,

@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsparse_indexer.so")
-SOURCES = ["api.hip", "score.hip", "topk.hip", "witness.hip", "block_select.hip", "dosa.hip"]
+SOURCES = ["api.hip", "score.hip", "topk.hip", "witness.hip", "block_select.hip", "dosa.hip",
+           "prior.hip"]
 ARCH = os.environ.get("SI_OFFLOAD_ARCH", "gfx950")
 
 COMMON = ["hipcc", f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

@@ -151,6 +151,45 @@ si_status idx_score_topk(const void* q, si_dtype q_dtype, const void* k, si_dtyp
   return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
 }
 
+size_t idx_score_topk_prior_workspace(int32_t n_q, int64_t max_vis, int32_t topk) {
+  if (n_q <= 0 || max_vis <= 0 || max_vis > INT32_MAX || topk < 1 || topk > kMaxTopk) return 0;
+  return prior_workspace_bytes(n_q, max_vis, topk);
+}
+
+si_status idx_score_topk_prior(const void* q, si_dtype q_dtype, const void* k, si_dtype k_dtype,
+                               const float* k_scale, const float* w, int64_t w_row_stride,
+                               const int64_t* k_row_offset, const int32_t* vis_len, int32_t n_q,
+                               int32_t H, int32_t D, int64_t n_k, int64_t max_vis, int32_t topk,
+                               const int32_t* prior_ids, int32_t prior_width, int32_t* out_idx,
+                               float* out_score, float* out_tau, int32_t* out_survivors,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ScoreArgs sa;
+  si_status s = check_score_args(q, q_dtype, k, k_dtype, k_scale, w, w_row_stride, k_row_offset,
+                                 vis_len, n_q, H, D, n_k, max_vis, &sa);
+  if (s != SI_OK) return s;
+  if (topk < 1 || topk > kMaxTopk || prior_width < 1 || prior_width > SI_MAX_PRIOR_WIDTH)
+    return SI_ERR_INVALID_ARGUMENT;
+  // the decode layout on the MFMA path: per-row keys, bf16 queries
+  if (q_dtype != SI_BF16 || k_dtype == SI_F32 || !score_mfma_supported(sa))
+    return SI_ERR_UNSUPPORTED_DTYPE;
+  if (n_q == 0) return SI_OK;
+  if (!k_row_offset || !prior_ids || !out_idx || !aligned4(out_idx) ||
+      (out_score && !aligned4(out_score)) || (out_tau && !aligned4(out_tau)) ||
+      (out_survivors && !aligned4(out_survivors)) || !aligned4(prior_ids))
+    return SI_ERR_INVALID_ARGUMENT;
+  if (max_vis == 0) {  // nothing visible: the plain path writes the padding
+    return idx_score_topk(q, q_dtype, k, k_dtype, k_scale, w, w_row_stride, k_row_offset,
+                          vis_len, n_q, H, D, n_k, max_vis, topk, out_idx, out_score, workspace,
+                          workspace_bytes, stream);
+  }
+  const size_t need = idx_score_topk_prior_workspace(n_q, max_vis, topk);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return SI_ERR_WORKSPACE_TOO_SMALL;
+  hipError_t e = launch_prior_topk(sa, prior_ids, prior_width, topk, out_idx, out_score, out_tau,
+                                   out_survivors, workspace, stream);
+  return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
+}
+
 si_status kvwitness_merge(int32_t* topk_idx, int32_t rows, int32_t topk,
                           const int32_t* context_lens, int32_t num_segments, int32_t keep,
                           int32_t max_replacements, hipStream_t stream) {

@@ -15,6 +15,7 @@
 //    c > 0).  No reuse across rows, so keys go straight to registers.
 //  * score_generic: VALU fp32 path for fp32 inputs and shapes the MFMA
 //    kernels do not cover.
+#include "score_rows.hpp"
 #include "score_shared.hpp"
 
 namespace si {
@@ -55,12 +56,12 @@ __global__ __launch_bounds__(256, 2) void score_mfma_shared(
 // ---------------------------------------------------------------------------
 constexpr int kRowsChunk = 4096;  // keys per workgroup
 
-template <int MT, int KS, bool FP8>
+template <int MT, int KS, bool FP8, bool FILT>
 __global__ __launch_bounds__(256, 2) void score_mfma_rows(
     const uint16_t* __restrict__ q, const void* __restrict__ kv, const float* __restrict__ kscale,
     const float* __restrict__ w, int64_t w_stride, const int64_t* __restrict__ row_off,
     const int32_t* __restrict__ vis_len, int n_q, int H, int64_t n_k, int64_t max_vis,
-    float* __restrict__ scores, int64_t score_stride) {
+    float* __restrict__ scores, int64_t score_stride, RowsFilter flt) {
   constexpr int D = 16 * KS;
   constexpr int ES = FP8 ? 1 : 2;        // bytes per key element
   constexpr int NL = FP8 ? KS / 2 : KS;  // 16-byte loads per lane per tile
@@ -74,22 +75,8 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows(
 
   bf16x8 a[1][MT][KS];
   float wv[MT][16];
-  {
-    const int hf = lane >> 5;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      int h = mt * 32 + (lane & 31);
-      bool ok = h < H;
-      const u32x4* src =
-          reinterpret_cast<const u32x4*>(q + ((int64_t)r * H + (ok ? h : 0)) * D + hf * (D / 2));
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        u32x4 x = ok ? src[s] : u32x4{0u, 0u, 0u, 0u};
-        a[0][mt][s] = as_bf16x8(x);
-      }
-    }
-    load_w_frag<MT>(w, w_stride, r, H, true, wv);
-  }
+  load_rows_frags<MT, KS>(q, w, w_stride, r, H, a, wv);
+  const float tr = FILT ? flt.tau[r] : 0.0f;
 
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(reinterpret_cast<const char*>(kv) + (off + c0) * D * ES), (short)0, nk * D * ES,
@@ -109,29 +96,15 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows(
              : 1.0f;
   };
   auto compute = [&](int tt, const u32x4 (&raw)[NL], float sc) {
-    f32x16 acc[1][MT];
-    mfma_tiles<1, MT, KS>(
-        a,
-        [&](int s) {
-          if (FP8) {
-            u32x4 bb;
-#pragma unroll
-            for (int hw = 0; hw < 2; ++hw) {
-              const uint32_t word = raw[s / 2][2 * (s % 2) + hw];
-              auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false);
-              auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true);
-              bb[2 * hw + 0] = __builtin_bit_cast(uint32_t, p0);
-              bb[2 * hw + 1] = __builtin_bit_cast(uint32_t, p1);
-            }
-            return as_bf16x8(bb);
-          }
-          return as_bf16x8(raw[s]);
-        },
-        acc);
-    float s = head_reduce<MT>(acc[0], wv);
-    if (FP8) s *= sc;
+    const float s = rows_tile_score<MT, KS, FP8>(a, wv, raw, sc);
     // lanes 32-63 hold the same sums; their out-of-range offset drops them
-    const int o = lane < 32 ? (tt + lane) * 4 : INT32_MAX;
+    int o = lane < 32 ? (tt + lane) * 4 : INT32_MAX;
+    if (FILT) {
+      const bool keep = lane < 32 && tt + lane < nk && s >= tr;
+      const uint64_t m = __ballot(keep);
+      if (lane == 0 && tt < nk) flt.bitmap[(int64_t)r * flt.words + ((c0 + tt) >> 5)] = (uint32_t)m;
+      o = keep ? o : INT32_MAX;
+    }
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s), ors, o, 0, 0);
   };
 
@@ -186,12 +159,13 @@ __device__ __forceinline__ void lds_load4(const void* g, uint32_t lds) {
                : "memory", "m0");
 }
 
-template <int MT, int KS>
+template <int MT, int KS, bool FILT>
 __global__ __launch_bounds__(256, 2) void score_mfma_rows_fp8(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
     const float* __restrict__ kscale, const float* __restrict__ w, int64_t w_stride,
     const int64_t* __restrict__ row_off, const int32_t* __restrict__ vis_len, int n_q, int H,
-    int64_t n_k, int64_t max_vis, float* __restrict__ scores, int64_t score_stride) {
+    int64_t n_k, int64_t max_vis, float* __restrict__ scores, int64_t score_stride,
+    RowsFilter flt) {
   constexpr int D = 16 * KS;
   constexpr int CPK = D / 16;      // 16-byte chunks per key
   constexpr int TB = 32 * D;       // bytes per 32-key tile
@@ -240,22 +214,8 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows_fp8(
   for (int i = 0; i < NB - 1; ++i) issue(i);
   bf16x8 a[1][MT][KS];
   float wv[MT][16];
-  {
-    const int hf = lane >> 5;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      int h = mt * 32 + (lane & 31);
-      bool ok = h < H;
-      const u32x4* src =
-          reinterpret_cast<const u32x4*>(q + ((int64_t)r * H + (ok ? h : 0)) * D + hf * (D / 2));
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        u32x4 x = ok ? src[s] : u32x4{0u, 0u, 0u, 0u};
-        a[0][mt][s] = as_bf16x8(x);
-      }
-    }
-    load_w_frag<MT>(w, w_stride, r, H, true, wv);
-  }
+  load_rows_frags<MT, KS>(q, w, w_stride, r, H, a, wv);
+  const float tr = FILT ? flt.tau[r] : 0.0f;
   const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(scores + (int64_t)r * score_stride + c0), (short)0, nk * 4, kBufWord3);
 
@@ -276,25 +236,16 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows_fp8(
       ch[j] = *reinterpret_cast<const u32x4*>(tb + 16 * (lk * CPK + (c ^ swz(lk))));
     }
     const float sc = sbuf[wave][i % NB][lk];
-    f32x16 acc[1][MT];
-    mfma_tiles<1, MT, KS>(
-        a,
-        [&](int s) {
-          u32x4 bb;
-#pragma unroll
-          for (int hw = 0; hw < 2; ++hw) {
-            const uint32_t word = ch[s / 2][2 * (s % 2) + hw];
-            auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false);
-            auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true);
-            bb[2 * hw + 0] = __builtin_bit_cast(uint32_t, p0);
-            bb[2 * hw + 1] = __builtin_bit_cast(uint32_t, p1);
-          }
-          return as_bf16x8(bb);
-        },
-        acc);
-    float s = head_reduce<MT>(acc[0], wv) * sc;
+    const float s = rows_tile_score<MT, KS, true>(a, wv, ch, sc);
     // lanes 32-63 hold the same sums; their out-of-range offset drops them
-    const int o = lane < 32 ? (first + 128 * i + lane) * 4 : INT32_MAX;
+    const int tt = first + 128 * i;
+    int o = lane < 32 ? (tt + lane) * 4 : INT32_MAX;
+    if (FILT) {
+      const bool keep = lane < 32 && tt + lane < nk && s >= tr;
+      const uint64_t m = __ballot(keep);
+      if (lane == 0 && tt < nk) flt.bitmap[(int64_t)r * flt.words + ((c0 + tt) >> 5)] = (uint32_t)m;
+      o = keep ? o : INT32_MAX;
+    }
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s), ors, o, 0, 0);
   }
   // no load may still be writing this wave's ring when the workgroup ends
@@ -370,6 +321,7 @@ static hipError_t launch_mfma(const ScoreArgs& a, const int32_t* row_list,
                       a.n_k * a.D * 2 <= (int64_t)INT32_MAX &&
                       a.max_vis * 4 <= (int64_t)INT32_MAX;
   if (row_list != nullptr && !shared) return hipErrorInvalidValue;
+  if (a.filter_tau != nullptr && shared) return hipErrorInvalidValue;  // decode layout only
   if (shared) {
     constexpr int QPW = (MT == 1) ? 2 : 1;
     const int groups = (a.n_q + 4 * QPW - 1) / (4 * QPW);
@@ -384,17 +336,28 @@ static hipError_t launch_mfma(const ScoreArgs& a, const int32_t* row_list,
   } else {
     const int64_t chunks = (a.max_vis + kRowsChunk - 1) / kRowsChunk;
     dim3 grid((unsigned)a.n_q, (unsigned)(chunks > 0 ? chunks : 1));
-    if (a.k_dtype == SI_FP8_E4M3FN)
-      hipLaunchKernelGGL((score_mfma_rows_fp8<MT, KS>), grid, dim3(256), 0, st,
-                         reinterpret_cast<const uint16_t*>(a.q),
-                         reinterpret_cast<const uint8_t*>(a.k), a.k_scale, a.w, a.w_row_stride,
-                         a.k_row_offset, a.vis_len, a.n_q, a.H, a.n_k, a.max_vis, a.scores,
-                         a.score_stride);
-    else
-      hipLaunchKernelGGL((score_mfma_rows<MT, KS, false>), grid, dim3(256), 0, st,
-                         reinterpret_cast<const uint16_t*>(a.q), a.k, a.k_scale, a.w,
-                         a.w_row_stride, a.k_row_offset, a.vis_len, a.n_q, a.H, a.n_k, a.max_vis,
-                         a.scores, a.score_stride);
+    const RowsFilter flt{a.filter_tau, a.filter_bitmap, a.filter_words};
+    const uint16_t* q16 = reinterpret_cast<const uint16_t*>(a.q);
+    if (a.k_dtype == SI_FP8_E4M3FN) {
+      const uint8_t* k8 = reinterpret_cast<const uint8_t*>(a.k);
+      if (flt.tau)
+        hipLaunchKernelGGL((score_mfma_rows_fp8<MT, KS, true>), grid, dim3(256), 0, st, q16, k8,
+                           a.k_scale, a.w, a.w_row_stride, a.k_row_offset, a.vis_len, a.n_q, a.H,
+                           a.n_k, a.max_vis, a.scores, a.score_stride, flt);
+      else
+        hipLaunchKernelGGL((score_mfma_rows_fp8<MT, KS, false>), grid, dim3(256), 0, st, q16, k8,
+                           a.k_scale, a.w, a.w_row_stride, a.k_row_offset, a.vis_len, a.n_q, a.H,
+                           a.n_k, a.max_vis, a.scores, a.score_stride, flt);
+    } else {
+      if (flt.tau)
+        hipLaunchKernelGGL((score_mfma_rows<MT, KS, false, true>), grid, dim3(256), 0, st, q16,
+                           a.k, a.k_scale, a.w, a.w_row_stride, a.k_row_offset, a.vis_len, a.n_q,
+                           a.H, a.n_k, a.max_vis, a.scores, a.score_stride, flt);
+      else
+        hipLaunchKernelGGL((score_mfma_rows<MT, KS, false, false>), grid, dim3(256), 0, st, q16,
+                           a.k, a.k_scale, a.w, a.w_row_stride, a.k_row_offset, a.vis_len, a.n_q,
+                           a.H, a.n_k, a.max_vis, a.scores, a.score_stride, flt);
+    }
   }
   return hipGetLastError();
 }

@@ -183,9 +183,20 @@ struct ScoreArgs {
   int64_t n_k, max_vis;
   float* scores;        // [n_q, score_stride]
   int64_t score_stride;
+  // optional (per-row keys only): keep s >= filter_tau[r]; survivor masks
+  // per 32-key tile in filter_bitmap [n_q, filter_words], scores stored for
+  // survivors only
+  const float* filter_tau = nullptr;
+  uint32_t* filter_bitmap = nullptr;
+  int64_t filter_words = 0;
 };
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
 bool score_mfma_supported(const ScoreArgs& a);
+// Decode top-K with a prior threshold (per-row keys on the MFMA path).
+size_t prior_workspace_bytes(int64_t n_q, int64_t max_vis, int K);
+hipError_t launch_prior_topk(const ScoreArgs& sa, const int32_t* prior, int prior_width, int K,
+                             int32_t* out_idx, float* out_score, float* out_tau,
+                             int32_t* out_count, void* ws, hipStream_t st);
 
 struct TopkArgs {
   const float* scores;  // row r at scores + r * stride

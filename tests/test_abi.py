@@ -118,6 +118,48 @@ def test_idx_score_topk_refusals(L):
     np.testing.assert_array_equal(outs, 7.0)
 
 
+def test_idx_score_topk_prior_refusals(L):
+    n_q, H, D, n_k, K, P = 4, 64, 128, 100, 16, 16
+    q = np.zeros(n_q * H * D + 8, np.uint16)
+    k = np.zeros(n_k * D + 16, np.uint8)
+    ks = np.ones(n_k, np.float32)
+    w = np.zeros(n_q * H, np.float32)
+    vis = np.full(n_q, 25, np.int32)
+    off = np.arange(n_q, dtype=np.int64) * 25
+    prior = np.zeros(n_q * P, np.int32)
+    out = np.full(n_q * K, 7, np.int32)
+    ws_need = L.idx_score_topk_prior_workspace(n_q, 25, K)
+    assert ws_need >= n_q * 25 * 4 * 3  # sparse scores + candidate ids + scores
+    assert L.idx_score_topk_prior_workspace(0, 25, K) == 0
+    ws = np.zeros(16, np.uint8)
+
+    def al(a):  # 16-byte aligned view start
+        return a.ctypes.data + (-a.ctypes.data) % 16
+
+    base = dict(q=al(q), qd=1, k=al(k), kd=2, ks=_p(ks), w=_p(w), ws_=H, off=_p(off),
+                vis=_p(vis), n_q=n_q, H=H, D=D, n_k=n_k, mv=25, K=K, pr=_p(prior), pw=P,
+                oi=_p(out), wsp=_p(ws), wsb=16)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.idx_score_topk_prior(a["q"], a["qd"], a["k"], a["kd"], a["ks"], a["w"], a["ws_"],
+                                      a["off"], a["vis"], a["n_q"], a["H"], a["D"], a["n_k"],
+                                      a["mv"], a["K"], a["pr"], a["pw"], a["oi"], None, None, None,
+                                      a["wsp"], a["wsb"], None)
+
+    assert call(pw=0) == INVALID
+    assert call(pw=2049) == INVALID
+    assert call(K=0) == INVALID
+    assert call(qd=0) == DTYPE  # fp32 queries: not the decode MFMA layout
+    assert call(kd=0) == DTYPE  # fp32 keys
+    assert call(D=96) == DTYPE  # the generic shape path has no decode layout
+    assert call(off=None) == INVALID  # shared keys: not the decode layout
+    assert call(pr=None) == INVALID
+    assert call() == WS
+    assert call(n_q=0) == OK
+    np.testing.assert_array_equal(out, 7)
+
+
 def test_block_select_refusals(L):
     q = np.zeros(64, np.float32)
     k = np.zeros(64, np.float32)
