@@ -212,10 +212,65 @@ def bench_indexer(args, cfg, workload):
                            key_dtype={0: "f32", 1: "bf16", 2: "fp8_e4m3fn"}[cfg["k_dtype"]],
                            pairs_per_step=pairs),
                roofline=roof, kernels=kern, event_ms_per_step=step_ms)
+    if workload == "decode":
+        out["prior_path"] = bench_prior(args, cfg, d, out_idx, wit)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline_rows(cfg, args.cpu_seconds, wit)
     return out
+
+
+PRIOR_EPS = 0.3  # query perturbation standing in for the previous decode step
+
+
+def bench_prior(args, cfg, d, ref_idx, wit):
+    """The same decode step through idx_score_topk_prior.  The prior is the
+    top-K of the previous step, stood in for by the plain top-K of the queries
+    plus PRIOR_EPS * N(0, 1) noise (seeded), computed before the timed region.
+    Checks that the ids equal the plain path's."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_indexer_02_amd as si
+    n_q, H, D, K, mv = cfg["n_q"], cfg["H"], cfg["D"], cfg["topk"], cfg["max_vis"]
+    dev = d["q"].device
+    g = torch.Generator(device="cpu").manual_seed(11)
+    qp = (d["q"].float() + PRIOR_EPS * torch.randn(d["q"].shape, generator=g).to(dev))
+    qp = qp.to(torch.bfloat16).contiguous()
+    prior, _ = si.idx_score_topk(qp, d["k"], d["w"], d["vis_len"], K, k_scale=d["k_scale"],
+                                 k_row_offset=d["k_row_offset"], max_vis=mv, want_scores=False)
+    out_idx = torch.empty((n_q, K), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(si.lib().idx_score_topk_prior_workspace(n_q, mv, K), 1),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        si.idx_score_topk_prior(d["q"], d["k"], d["w"], d["vis_len"], K, prior,
+                                k_scale=d["k_scale"], k_row_offset=d["k_row_offset"],
+                                max_vis=mv, out_idx=out_idx, want_scores=False, workspace=ws)
+
+    def witness():
+        si.kvwitness_merge(out_idx, d["vis_len"], wit["S"], wit["keep"], wit["max_rep"])
+
+    wall_ms, per = timed_steps([("score_topk_prior", step), ("witness", witness)], args.steps,
+                               args.warmup)
+    # (the timed output went through the witness merge; compare fresh ids)
+    pid, _, (tau, surv) = si.idx_score_topk_prior(
+        d["q"], d["k"], d["w"], d["vis_len"], K, prior, k_scale=d["k_scale"],
+        k_row_offset=d["k_row_offset"], max_vis=mv, want_scores=False, want_stats=True)
+    plain, _ = si.idx_score_topk(d["q"], d["k"], d["w"], d["vis_len"], K, k_scale=d["k_scale"],
+                                 k_row_offset=d["k_row_offset"], max_vis=mv, want_scores=False)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(plain, pid))
+    # share of this step's selected ids that the prior also holds, per row
+    pr, pl = prior.cpu().numpy(), plain.cpu().numpy()
+    overlap = float(np.mean([np.intersect1d(a[a >= 0], b[b >= 0]).size / max(1, int((b >= 0).sum()))
+                             for a, b in zip(pr, pl)]))
+    vis = np.minimum(cfg["vis_len"].astype(np.int64), mv)
+    return dict(ms_per_step=wall_ms, stage_ms={k: v for k, v in per.items()},
+                ids_equal_plain=same, survivors=int(surv.sum().item()), visible=int(vis.sum()),
+                survival=float(surv.sum().item()) / float(vis.sum()),
+                prior=f"plain top-K of q + {PRIOR_EPS} N(0,1) (seed 11); "
+                      f"it holds {overlap:.3f} of this step's selected ids")
 
 
 def workload_name(cfg, workload):

@@ -54,7 +54,6 @@ __global__ __launch_bounds__(256, 2) void score_mfma_shared(
 // resources bounded at the chunk's end (loads past it read zero, stores past
 // it are dropped), so neither loads nor stores sit under a branch.
 // ---------------------------------------------------------------------------
-constexpr int kRowsChunk = 4096;  // keys per workgroup
 
 template <int MT, int KS, bool FP8, bool FILT>
 __global__ __launch_bounds__(256, 2) void score_mfma_rows(
@@ -77,6 +76,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows(
   float wv[MT][16];
   load_rows_frags<MT, KS>(q, w, w_stride, r, H, a, wv);
   const float tr = FILT ? flt.tau[r] : 0.0f;
+  int kept = 0;  // survivors this wave stored (filter only)
 
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(reinterpret_cast<const char*>(kv) + (off + c0) * D * ES), (short)0, nk * D * ES,
@@ -103,6 +103,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows(
       const bool keep = lane < 32 && tt + lane < nk && s >= tr;
       const uint64_t m = __ballot(keep);
       if (lane == 0 && tt < nk) flt.bitmap[(int64_t)r * flt.words + ((c0 + tt) >> 5)] = (uint32_t)m;
+      kept += __builtin_popcountll(m);
       o = keep ? o : INT32_MAX;
     }
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s), ors, o, 0, 0);
@@ -123,6 +124,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows(
     compute(first + 128 * (i + 1), rb, sb);
   }
   if (i < n_i) compute(first + 128 * i, ra, sa);
+  if (FILT) filter_chunk_count(flt, r, kept);
 }
 
 // ---------------------------------------------------------------------------
@@ -160,7 +162,7 @@ __device__ __forceinline__ void lds_load4(const void* g, uint32_t lds) {
 }
 
 template <int MT, int KS, bool FILT>
-__global__ __launch_bounds__(256, 2) void score_mfma_rows_fp8(
+__global__ __launch_bounds__(256, 3) void score_mfma_rows_fp8(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
     const float* __restrict__ kscale, const float* __restrict__ w, int64_t w_stride,
     const int64_t* __restrict__ row_off, const int32_t* __restrict__ vis_len, int n_q, int H,
@@ -216,6 +218,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows_fp8(
   float wv[MT][16];
   load_rows_frags<MT, KS>(q, w, w_stride, r, H, a, wv);
   const float tr = FILT ? flt.tau[r] : 0.0f;
+  int kept = 0;  // survivors this wave stored (filter only)
   const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(scores + (int64_t)r * score_stride + c0), (short)0, nk * 4, kBufWord3);
 
@@ -244,12 +247,14 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows_fp8(
       const bool keep = lane < 32 && tt + lane < nk && s >= tr;
       const uint64_t m = __ballot(keep);
       if (lane == 0 && tt < nk) flt.bitmap[(int64_t)r * flt.words + ((c0 + tt) >> 5)] = (uint32_t)m;
+      kept += __builtin_popcountll(m);
       o = keep ? o : INT32_MAX;
     }
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s), ors, o, 0, 0);
   }
   // no load may still be writing this wave's ring when the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (FILT) filter_chunk_count(flt, r, kept);
 }
 
 // ---------------------------------------------------------------------------
@@ -321,7 +326,9 @@ static hipError_t launch_mfma(const ScoreArgs& a, const int32_t* row_list,
                       a.n_k * a.D * 2 <= (int64_t)INT32_MAX &&
                       a.max_vis * 4 <= (int64_t)INT32_MAX;
   if (row_list != nullptr && !shared) return hipErrorInvalidValue;
-  if (a.filter_tau != nullptr && shared) return hipErrorInvalidValue;  // decode layout only
+  if (a.filter_tau != nullptr &&
+      (shared || a.filter_bitmap == nullptr || a.filter_chunk_cnt == nullptr))
+    return hipErrorInvalidValue;  // decode layout only, with both outputs
   if (shared) {
     constexpr int QPW = (MT == 1) ? 2 : 1;
     const int groups = (a.n_q + 4 * QPW - 1) / (4 * QPW);
@@ -336,7 +343,8 @@ static hipError_t launch_mfma(const ScoreArgs& a, const int32_t* row_list,
   } else {
     const int64_t chunks = (a.max_vis + kRowsChunk - 1) / kRowsChunk;
     dim3 grid((unsigned)a.n_q, (unsigned)(chunks > 0 ? chunks : 1));
-    const RowsFilter flt{a.filter_tau, a.filter_bitmap, a.filter_words};
+    const RowsFilter flt{a.filter_tau, a.filter_bitmap, a.filter_words, a.filter_chunk_cnt,
+                         chunks};
     const uint16_t* q16 = reinterpret_cast<const uint16_t*>(a.q);
     if (a.k_dtype == SI_FP8_E4M3FN) {
       const uint8_t* k8 = reinterpret_cast<const uint8_t*>(a.k);

@@ -65,11 +65,22 @@ __device__ __forceinline__ float rows_tile_score(const bf16x8 (&a)[1][MT][KS],
 
 // Optional score filter of the decode kernels: keep s >= tau[r]; each
 // 32-key tile writes its survivor mask to bitmap[r * words + key / 32] and
-// stores only the survivors' scores.
+// stores only the survivors' scores; each workgroup (row r, key chunk c)
+// writes its survivor count to chunk_cnt[r * chunks + c].
 struct RowsFilter {
   const float* tau;
   uint32_t* bitmap;
   int64_t words;
+  int32_t* chunk_cnt;
+  int64_t chunks;
 };
+
+// Each wave's survivor count of the workgroup's key chunk, at
+// chunk_cnt[(r * chunks + chunk) * 4 + wave] (no barrier, so a wave that
+// is done leaves at once).
+__device__ __forceinline__ void filter_chunk_count(const RowsFilter& flt, int r, int count) {
+  if ((threadIdx.x & 63) == 0)
+    flt.chunk_cnt[((int64_t)r * flt.chunks + blockIdx.y) * 4 + (threadIdx.x >> 6)] = count;
+}
 
 }  // namespace si

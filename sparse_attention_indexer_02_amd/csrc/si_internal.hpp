@@ -185,11 +185,16 @@ struct ScoreArgs {
   int64_t score_stride;
   // optional (per-row keys only): keep s >= filter_tau[r]; survivor masks
   // per 32-key tile in filter_bitmap [n_q, filter_words], scores stored for
-  // survivors only
+  // survivors only, survivor counts per key chunk and wave in
+  // filter_chunk_cnt [n_q, rows_key_chunks(max_vis), 4]
   const float* filter_tau = nullptr;
   uint32_t* filter_bitmap = nullptr;
   int64_t filter_words = 0;
+  int32_t* filter_chunk_cnt = nullptr;
 };
+// Keys per workgroup of the per-row (decode layout) score kernels.
+constexpr int64_t kRowsChunk = 4096;
+inline int64_t rows_key_chunks(int64_t max_vis) { return (max_vis + kRowsChunk - 1) / kRowsChunk; }
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
 bool score_mfma_supported(const ScoreArgs& a);
 // Decode top-K with a prior threshold (per-row keys on the MFMA path).
@@ -222,6 +227,12 @@ struct TopkArgs {
 // top-K lists are selected from again (needs topk_workspace_bytes of
 // workspace; without it, or for K > 2048, a single-workgroup radix select).
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+// The one-workgroup block top-K's limits (rows of at most this many scores,
+// K at most this).
+constexpr int kBlockTopkMaxN = 8192;
+constexpr int kBlockTopkMaxK = 2048;
+// Always the single-workgroup radix select (any length, any K <= kMaxTopk).
+hipError_t launch_topk_generic(const TopkArgs& a, hipStream_t st);
 size_t topk_workspace_bytes(int64_t n_rows, int64_t max_vis, int K);
 constexpr int kMaxTopk = 4096;
 hipError_t launch_score_rows_listed(const ScoreArgs& a, const int32_t* row_list,

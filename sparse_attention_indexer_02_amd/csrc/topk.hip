@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkArgs a) {
     if (t < cnt) {
       uint64_t c = sortbuf[t];
       uint32_t idx = comp_idx(c);
-      oi[t] = a.id_map ? a.id_map[idx] : (int32_t)idx;
+      oi[t] = a.id_map ? a.id_map[(int64_t)r * a.id_map_stride + idx] : (int32_t)idx;
       if (os) os[t] = key_to_float(comp_key(c));
     } else {
       oi[t] = -1;
@@ -137,6 +137,12 @@ size_t topk_workspace_bytes(int64_t n_rows, int64_t max_vis, int K) {
   size_t total = 0;
   for (int64_t len = max_vis; len > kBN; len = chunks_of(len) * K) total += level_bytes(n_rows, len, K);
   return total;
+}
+
+hipError_t launch_topk_generic(const TopkArgs& a, hipStream_t st) {
+  if (a.n_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_rows, dim3((unsigned)a.n_rows), dim3(kTopkThreads), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {

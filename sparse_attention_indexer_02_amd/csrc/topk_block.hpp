@@ -35,9 +35,10 @@ namespace si {
 constexpr int kBT = 256;              // threads per row
 constexpr int kBPer = 32;             // positions per thread
 constexpr int kBN = kBT * kBPer;      // 8192
+static_assert(kBN == kBlockTopkMaxN, "block top-K row capacity");
 constexpr int kBGroups = kBPer / 4;   // float4 groups per thread
 constexpr int kBStep = 4 * kBT;       // positions per group row
-constexpr int kBK = 2048;             // largest K
+constexpr int kBK = kBlockTopkMaxK;   // largest K (2048)
 constexpr int kBins = 4096;           // value bins
 constexpr int kBinsPer = kBins / kBT;
 constexpr int kBrute = 256;           // largest b1 ranked item by item

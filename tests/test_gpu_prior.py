@@ -140,3 +140,25 @@ def test_prior_full_size(orc):
         v = orc.visible(kp, int(r))
         check_topk_row(ui[r], us[r], S[n, :v], M[n, :v], N[n, :v], cfg["topk"],
                        where=f"prior full-size row {r}")
+
+
+@pytest.mark.parametrize("lens", [[0, 3000, 1, 9000], [0, 600000, 5000, 1]])
+def test_prior_empty_and_long_rows(orc, lens):
+    """An empty row, a one-key row, and (second case) a row longer than the
+    per-row LDS bitmap of prior ids covers, which takes the one-workgroup
+    threshold kernel."""
+    cfg = synth.decode(seed=41, lens=lens, topk=256)
+    d = dev_inputs(cfg)
+    _check_equal(d, cfg, _perturbed_prior(d, cfg, 0.3, 4), "empty and long rows, perturbed prior")
+    exact, _ = _plain(d, cfg)
+    _check_equal(d, cfg, exact, "empty and long rows, exact prior")
+
+
+def test_prior_large_k(orc):
+    """K above the block top-K's 2048: every prior is narrower than K, so
+    tau is -inf and the radix select takes every row through the candidate
+    id map."""
+    cfg = _decode(seed=51, rows=6, max_len=9000, K=3000)
+    d = dev_inputs(cfg)
+    exact, _ = _plain(d, cfg)
+    _check_equal(d, cfg, exact[:, :2048].contiguous(), "K 3000, the first 2048 exact ids")
