@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256) void prior_kth(const float* __restrict__ prior
 // before it (chunk_cnt [n_q, chunks, 4]: the counts of a chunk's waves);
 // thread t takes keys t + 256 i of the chunk (coalesced reads of the
 // scores).  Workgroup (r, 0) records the row's count and lists rows
-// with more than kSmallCands survivors for the radix select.
+// with more than kSmallCands survivors for the chunked selection.
 __global__ __launch_bounds__(256) void prior_compact(
     const uint32_t* __restrict__ bitmap, int64_t words, const int32_t* __restrict__ chunk_cnt,
     int64_t chunks, const int32_t* __restrict__ vis_len, const int64_t* __restrict__ row_off,
@@ -312,10 +312,12 @@ __global__ void prior_zero(int32_t* p) { *p = 0; }
 
 // Workspace regions (256-byte aligned): tau, bitmap, per-chunk survivor
 // counts, the prior scores and their counts, sparse scores, the candidates,
-// counts, the overflow list.
+// counts, the overflow list, the chunked top-K's levels.
 struct PriorLayout {
-  size_t tau, bitmap, chunk_cnt, prior_sc, prior_m, sparse, cand_ids, cand_sc, counts, ovf, total;
+  size_t tau, bitmap, chunk_cnt, prior_sc, prior_m, sparse, cand_ids, cand_sc, counts, ovf,
+      topk_ws, total;
   int64_t words, chunks, cap;
+  size_t topk_ws_bytes;
 };
 static PriorLayout prior_layout(int64_t n_q, int64_t max_vis, int K) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -334,6 +336,9 @@ static PriorLayout prior_layout(int64_t n_q, int64_t max_vis, int K) {
   L.cand_sc = o; o += al((size_t)n_q * L.cap * 4);
   L.counts = o; o += al((size_t)n_q * 4);
   L.ovf = o; o += al((size_t)(n_q + 1) * 4);
+  L.topk_ws = o;
+  L.topk_ws_bytes = topk_workspace_bytes(n_q, L.cap, K);
+  o += al(L.topk_ws_bytes);
   L.total = o;
   return L;
 }
@@ -400,13 +405,15 @@ static hipError_t run_prior(const ScoreArgs& sa, const int32_t* prior, int pw, i
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // every row through one workgroup over its first kSmallCands survivors;
-  // rows with more (listed by prior_compact) are then redone by the
-  // single-workgroup radix select over all of them: one launch that ends at
-  // once when no row overflowed
+  // rows with more (listed by prior_compact) are then redone over all of
+  // them by the chunked selection (8192-survivor chunks, then merge levels),
+  // whose launches end at once when no row is listed
   TopkArgs ta;
   ta.scores = cand_sc; ta.stride = L.cap; ta.vis_len = counts; ta.k_row_offset = nullptr;
   ta.n_k = L.cap; ta.n_rows = sa.n_q; ta.K = K; ta.out_idx = out_idx; ta.out_score = out_score;
   ta.id_map = cand_ids; ta.id_map_stride = L.cap;
+  ta.workspace = ws + L.topk_ws;
+  ta.workspace_bytes = L.topk_ws_bytes;
   if (K <= kBlockTopkMaxK && L.cap > kSmallCands) {
     ta.max_vis = kSmallCands;
     e = launch_topk(ta, st);
@@ -415,10 +422,10 @@ static hipError_t run_prior(const ScoreArgs& sa, const int32_t* prior, int pw, i
     tb.max_vis = L.cap;
     tb.row_list = ovf;
     tb.row_count = ovf_n;
-    e = launch_topk_generic(tb, st);
+    e = launch_topk(tb, st);
   } else {
     ta.max_vis = L.cap;  // one workgroup per row takes it whole (larger K: the radix select)
-    e = K <= kBlockTopkMaxK ? launch_topk(ta, st) : launch_topk_generic(ta, st);
+    e = launch_topk(ta, st);
   }
   if (e != hipSuccess) return e;
   if (out_tau) {

@@ -231,8 +231,6 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 // K at most this).
 constexpr int kBlockTopkMaxN = 8192;
 constexpr int kBlockTopkMaxK = 2048;
-// Always the single-workgroup radix select (any length, any K <= kMaxTopk).
-hipError_t launch_topk_generic(const TopkArgs& a, hipStream_t st);
 size_t topk_workspace_bytes(int64_t n_rows, int64_t max_vis, int K);
 constexpr int kMaxTopk = 4096;
 hipError_t launch_score_rows_listed(const ScoreArgs& a, const int32_t* row_list,

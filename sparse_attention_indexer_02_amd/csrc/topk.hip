@@ -139,12 +139,6 @@ size_t topk_workspace_bytes(int64_t n_rows, int64_t max_vis, int K) {
   return total;
 }
 
-hipError_t launch_topk_generic(const TopkArgs& a, hipStream_t st) {
-  if (a.n_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_rows, dim3((unsigned)a.n_rows), dim3(kTopkThreads), 0, st, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.n_rows == 0) return hipSuccess;
   const dim3 grid((unsigned)a.n_rows);
