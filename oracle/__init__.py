@@ -74,6 +74,8 @@ def lib():
             "orc_block_select_rows": (None, [vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, i32,
                                              i32, vp, i32, vp]),
             "orc_positions_of_blocks": (i64, [vp, i32, i64, i64, i32, vp]),
+            "orc_positions_of_block_rows": (None, [vp, i32, i32, i32, vp, i64, i32, vp, i64, vp]),
+            "orc_gather_slots": (None, [vp, i32, i32, vp, vp, vp, i32, i32, vp]),
             "orc_dosa_common_prefix": (i32, [vp]),
             "orc_dosa_rep_row": (i32, [i32, i32, i32]),
             "orc_dosa_seeds": (i32, [vp, vp, vp, vp]),
@@ -247,6 +249,32 @@ def positions_of_blocks(blocks, query_pos, n_pos, block_size):
     out = np.empty(max(len(b) * block_size, 1), dtype=np.int64)
     n = lib().orc_positions_of_blocks(_p(b), len(b), query_pos, n_pos, block_size, _p(out))
     return list(out[:n])
+
+
+def positions_of_block_rows(blocks, query_pos, n_pos, block_size, out_width):
+    """blocks [n_q, n_heads, width] i32 -> (positions [n_q, n_heads, out_width] i32 with -1
+    after the covered ones, counts [n_q, n_heads] i32)."""
+    b = np.ascontiguousarray(blocks, dtype=np.int32)
+    n_q, n_heads, width = b.shape
+    qp = np.ascontiguousarray(query_pos, dtype=np.int64)
+    out = np.empty((n_q, n_heads, out_width), dtype=np.int32)
+    cnt = np.empty((n_q, n_heads), dtype=np.int32)
+    lib().orc_positions_of_block_rows(_p(b), n_q, n_heads, width, _p(qp), n_pos, block_size,
+                                      _p(out), out_width, _p(cnt))
+    return out, cnt
+
+
+def gather_slots(idx, lens, *, row_start=None, page_table=None, page_size=0):
+    """idx [rows, width] i32 row-relative entries -> KV slots [rows, width] i64 (-1: none)."""
+    x = np.ascontiguousarray(idx, dtype=np.int32)
+    rows, width = x.shape
+    ln = np.ascontiguousarray(lens, dtype=np.int32)
+    rs = None if row_start is None else np.ascontiguousarray(row_start, dtype=np.int64)
+    pt = None if page_table is None else np.ascontiguousarray(page_table, dtype=np.int32)
+    ppr = 0 if pt is None else pt.shape[1]
+    out = np.empty((rows, width), dtype=np.int64)
+    lib().orc_gather_slots(_p(x), rows, width, _p(ln), _p(rs), _p(pt), ppr, page_size, _p(out))
+    return out
 
 
 def dosa_params(n_seeds, n_rep_queries=4, rep_topk=2048, kept_heads=16, neg_active_frac=0.5,

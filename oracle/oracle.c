@@ -456,11 +456,14 @@ void orc_block_select_rows(const float* q, const float* k, const int64_t* query_
 }
 
 /* [BLOCK] positions_of_blocks: covered positions, ascending, causally
- * clipped, deduplicated.  Returns the count written to out. */
+ * clipped, deduplicated.  Returns the count written to out.  A negative
+ * entry is the -1 padding of an i32 block list and covers nothing (the
+ * page's lists are unsigned and unpadded). */
 int64_t orc_positions_of_blocks(const int32_t* blocks, int32_t n_sel, int64_t query_pos,
                                 int64_t n_pos, int32_t block_size, int64_t* out) {
   int64_t n = 0;
   for (int32_t i = 0; i < n_sel; ++i) {
+    if (blocks[i] < 0) continue;
     int64_t start = (int64_t)blocks[i] * block_size;
     int64_t end = start + block_size;
     if (end > n_pos) end = n_pos;
@@ -480,6 +483,58 @@ int64_t orc_positions_of_blocks(const int32_t* blocks, int32_t n_sel, int64_t qu
   for (int64_t i = 0; i < n; ++i)
     if (m == 0 || out[m - 1] != out[i]) out[m++] = out[i];
   return m;
+}
+
+/* positions_of_blocks over [n_q, n_heads, width] block lists (query q's
+ * lists share query_pos[q]): list l's positions as i32 in out[l * out_width
+ * ..], -1 after the count[l] covered ones.  out_width must hold every
+ * position the list can cover. */
+void orc_positions_of_block_rows(const int32_t* blocks, int32_t n_q, int32_t n_heads,
+                                 int32_t width, const int64_t* query_pos, int64_t n_pos,
+                                 int32_t block_size, int32_t* out, int64_t out_width,
+                                 int32_t* count) {
+  int64_t* tmp = (int64_t*)malloc(sizeof(int64_t) * (size_t)(width * (int64_t)block_size + 1));
+  for (int64_t l = 0; l < (int64_t)n_q * n_heads; ++l) {
+    int64_t m = orc_positions_of_blocks(blocks + l * width, width, query_pos[l / n_heads], n_pos,
+                                        block_size, tmp);
+    for (int64_t i = 0; i < out_width; ++i) out[l * out_width + i] = i < m ? (int32_t)tmp[i] : -1;
+    count[l] = (int32_t)m;
+  }
+  free(tmp);
+}
+
+/* Gather slots for the attention that consumes a selection row.  [WIT]
+ * Coordinates: entries are row-relative offsets with valid range [0, L_r);
+ * -1 is padding, and a learned entry >= L_r passes through the merge but
+ * names no token of the row.  So entry x of row r is gathered iff
+ * 0 <= x < L_r, and every other entry maps to -1.  A gathered x lives at
+ *   row_start[r] + x                                  (flat KV buffer), or
+ *   page_table[r][x / page_size] * page_size + x % page_size   (paged KV: a
+ *   page holds page_size consecutive tokens; [BLOCK] module docs make the
+ *   128-token block the KV page),
+ * and -1 when x's page lies past pages_per_row or its page id is negative.
+ * Exactly one of row_start / page_table is non-NULL. */
+void orc_gather_slots(const int32_t* idx, int32_t rows, int32_t width, const int32_t* lens,
+                      const int64_t* row_start, const int32_t* page_table, int32_t pages_per_row,
+                      int32_t page_size, int64_t* out) {
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t i = 0; i < width; ++i) {
+      const int64_t x = idx[r * width + i];
+      int64_t slot = -1;
+      if (x >= 0 && x < (int64_t)lens[r]) {
+        if (row_start) {
+          slot = row_start[r] + x;
+        } else {
+          const int64_t pg = x / page_size;
+          if (pg < pages_per_row) {
+            const int64_t id = page_table[r * pages_per_row + pg];
+            if (id >= 0) slot = id * page_size + x % page_size;
+          }
+        }
+      }
+      out[r * width + i] = slot;
+    }
+  }
 }
 
 /* ------------------------------------------------------------------------ */

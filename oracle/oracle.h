@@ -101,6 +101,13 @@ void orc_block_select_rows(const float* q /*[n_q,H,D]*/, const float* k, const i
                            int32_t width, int32_t* counts);
 int64_t orc_positions_of_blocks(const int32_t* blocks, int32_t n_blocks_sel, int64_t query_pos,
                                 int64_t n_pos, int32_t block_size, int64_t* out);
+void orc_positions_of_block_rows(const int32_t* blocks, int32_t n_q, int32_t n_heads,
+                                 int32_t width, const int64_t* query_pos, int64_t n_pos,
+                                 int32_t block_size, int32_t* out, int64_t out_width,
+                                 int32_t* count);
+void orc_gather_slots(const int32_t* idx, int32_t rows, int32_t width, const int32_t* lens,
+                      const int64_t* row_start, const int32_t* page_table, int32_t pages_per_row,
+                      int32_t page_size, int64_t* out);
 
 /* ---- DoSA certified prune ---- */
 typedef struct {
