@@ -9,6 +9,8 @@
  *   dosa_prune_topk      the same top-K through DoSA's certified prune
  *   kvwitness_merge      segment-witness covering merge, in place
  *   block_sparse_select  MiniMax-M3 block-sparse block selection
+ *   positions_of_blocks  the positions a block selection covers
+ *   gather_slots         KV slots of a selection row (flat or paged KV)
  *
  * Conventions shared by every call:
  *  - Tensor arguments are DEVICE pointers owned by the caller.  The library
@@ -297,6 +299,61 @@ si_status block_sparse_select(const float* index_q, const float* index_k,
                               size_t workspace_bytes, hipStream_t stream);
 size_t block_sparse_select_workspace(int32_t n_q, int32_t n_kv_heads, int64_t n_pos,
                                      int32_t block_size);
+
+/* ------------------------------------------------------------------------ *
+ * positions_of_blocks
+ *
+ * ferrox_core block_sparse.rs (docs.rs, ferrox-core 0.14.0), fn
+ * positions_of_blocks: the positions a block list covers, ascending and
+ * deduplicated, each block b covering [b*bs, min((b+1)*bs, n_pos, p+1))
+ * for the query at p = query_pos[i] (nothing when p < 0).  Negative entries
+ * are padding and cover nothing; the list may be in any order and repeat
+ * blocks.
+ *
+ *  blocks    [n_q, n_kv_heads, width] i32 (e.g. block_sparse_select's
+ *            out_blocks), 0 <= width <= 4096.
+ *  query_pos [n_q] i64, shared by the query's KV heads.
+ *  out_pos   [n_q, n_kv_heads, out_width] i32: the covered positions, then
+ *            -1.  out_width >= min(width * block_size, n_pos), so every
+ *            covered position fits.
+ *  out_count [n_q, n_kv_heads] i32 (may be NULL): positions covered.
+ * Errors: INVALID_ARGUMENT (negative counts, block_size < 1, width > 4096,
+ * n_pos outside [0, 2^31 - 1], out_width too small, null pointers).
+ * ------------------------------------------------------------------------ */
+si_status positions_of_blocks(const int32_t* blocks, int32_t n_q, int32_t n_kv_heads,
+                              int32_t width, const int64_t* query_pos, int64_t n_pos,
+                              int32_t block_size, int32_t* out_pos, int32_t out_width,
+                              int32_t* out_count, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * gather_slots
+ *
+ * Where the attention that consumes a selection row reads each entry.  The
+ * "Segment Witnesses" page (Implementation rule and contracts: Coordinates)
+ * makes the entries of a (witness-merged) top-K row row-relative offsets:
+ * row r's tokens are [0, L_r), -1 is padding, and a learned entry >= L_r
+ * passes through the merge without naming a token of the row.  Entry x of
+ * row r is gathered iff 0 <= x < L_r, at
+ *   row_start[r] + x                                    (flat KV buffer), or
+ *   page_table[r][x / page_size] * page_size + x % page_size   (paged KV; the
+ *   block-sparse page makes its 128-token block the KV page),
+ * and every other entry, a page index >= pages_per_row and a negative page
+ * id give -1.  The row's order is kept.
+ *
+ *  idx        [rows, width] i32 (e.g. kvwitness_merge's output rows, or
+ *             positions_of_blocks' lists with L_r = n_pos).
+ *  lens       [rows] i32: L_r.
+ *  row_start  [rows] i64, or NULL when page_table is given (exactly one).
+ *  page_table [rows, pages_per_row] i32 physical page ids.
+ *  out_slots  [rows, width] i64.
+ * Errors: INVALID_ARGUMENT (negative counts, both or neither mapping,
+ * page_size or pages_per_row < 1 with a page table, width > 2^26, null
+ * pointers).
+ * ------------------------------------------------------------------------ */
+si_status gather_slots(const int32_t* idx, int32_t rows, int32_t width, const int32_t* lens,
+                       const int64_t* row_start, const int32_t* page_table,
+                       int32_t pages_per_row, int32_t page_size, int64_t* out_slots,
+                       hipStream_t stream);
 
 const char* si_status_string(si_status status);
 

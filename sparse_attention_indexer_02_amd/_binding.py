@@ -58,6 +58,8 @@ SIGNATURES = {
     "block_sparse_select": (i32, [vp, vp, vp, i32, i32, i32, i64, i32, i32, i32, i32, vp, i32, vp,
                                   vp, sz, vp]),
     "block_sparse_select_workspace": (sz, [i32, i32, i64, i32]),
+    "positions_of_blocks": (i32, [vp, i32, i32, i32, vp, i64, i32, vp, i32, vp, vp]),
+    "gather_slots": (i32, [vp, i32, i32, vp, vp, vp, i32, i32, vp, vp]),
     "si_status_string": (C.c_char_p, [i32]),
 }
 
@@ -325,3 +327,44 @@ def block_sparse_select(index_q, index_k, query_pos, *, block_size=128, top_bloc
                                    ws_bytes, _stream(dev))
     _check(st, "block_sparse_select")
     return out_blocks, out_count
+
+
+def positions_of_blocks(blocks, query_pos, n_pos, block_size, *, out_width=None, out_pos=None,
+                        out_count=None):
+    """Positions each (query, KV head) block list covers, ascending, deduplicated and
+    causally clipped, then -1; returns (out_pos [n_q, H, out_width] i32, out_count)."""
+    _dev_tensor(blocks, "blocks", torch.int32)
+    _dev_tensor(query_pos, "query_pos", torch.int64)
+    dev = blocks.device
+    n_q, H, width = blocks.shape
+    if out_width is None:
+        out_width = max(min(width * block_size, n_pos), 1)
+    if out_pos is None:
+        out_pos = torch.empty((n_q, H, out_width), dtype=torch.int32, device=dev)
+    if out_count is None:
+        out_count = torch.empty((n_q, H), dtype=torch.int32, device=dev)
+    st = lib().positions_of_blocks(_ptr(blocks), n_q, H, width, _ptr(query_pos), n_pos,
+                                   block_size, _ptr(out_pos), out_width, _ptr(out_count),
+                                   _stream(dev))
+    _check(st, "positions_of_blocks")
+    return out_pos, out_count
+
+
+def gather_slots(idx, lens, *, row_start=None, page_table=None, page_size=0, out=None):
+    """KV slots [rows, width] i64 of row-relative entries (-1 where an entry names no
+    token of its row), through row starts (flat KV) or a page table (paged KV)."""
+    _dev_tensor(idx, "idx", torch.int32)
+    _dev_tensor(lens, "lens", torch.int32)
+    if row_start is not None:
+        _dev_tensor(row_start, "row_start", torch.int64)
+    if page_table is not None:
+        _dev_tensor(page_table, "page_table", torch.int32)
+    dev = idx.device
+    rows, width = idx.shape
+    ppr = page_table.shape[1] if page_table is not None else 0
+    if out is None:
+        out = torch.empty((rows, width), dtype=torch.int64, device=dev)
+    st = lib().gather_slots(_ptr(idx), rows, width, _ptr(lens), _ptr(row_start), _ptr(page_table),
+                            ppr, page_size, _ptr(out), _stream(dev))
+    _check(st, "gather_slots")
+    return out

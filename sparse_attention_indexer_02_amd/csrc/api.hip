@@ -237,4 +237,37 @@ si_status block_sparse_select(const float* index_q, const float* index_k,
   return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
 }
 
+si_status positions_of_blocks(const int32_t* blocks, int32_t n_q, int32_t n_kv_heads,
+                              int32_t width, const int64_t* query_pos, int64_t n_pos,
+                              int32_t block_size, int32_t* out_pos, int32_t out_width,
+                              int32_t* out_count, hipStream_t stream) {
+  if (n_q < 0 || n_kv_heads < 0 || width < 0 || width > kMaxTopk || block_size < 1 ||
+      n_pos < 0 || n_pos > INT32_MAX || out_width < 0)
+    return SI_ERR_INVALID_ARGUMENT;
+  const int64_t most = (int64_t)width * block_size < n_pos ? (int64_t)width * block_size : n_pos;
+  if (out_width < most) return SI_ERR_INVALID_ARGUMENT;
+  if ((int64_t)n_q * n_kv_heads > INT32_MAX) return SI_ERR_INVALID_ARGUMENT;
+  if (n_q == 0 || n_kv_heads == 0) return SI_OK;
+  if (!query_pos || (out_width > 0 && !out_pos) || (width > 0 && !blocks))
+    return SI_ERR_INVALID_ARGUMENT;
+  hipError_t e = launch_block_positions(blocks, n_q, n_kv_heads, width, query_pos, n_pos,
+                                        block_size, out_pos, out_width, out_count, stream);
+  return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
+}
+
+si_status gather_slots(const int32_t* idx, int32_t rows, int32_t width, const int32_t* lens,
+                       const int64_t* row_start, const int32_t* page_table,
+                       int32_t pages_per_row, int32_t page_size, int64_t* out_slots,
+                       hipStream_t stream) {
+  if (rows < 0 || width < 0 || width > (1 << 26)) return SI_ERR_INVALID_ARGUMENT;
+  if ((row_start == nullptr) == (page_table == nullptr)) return SI_ERR_INVALID_ARGUMENT;
+  if (page_table && (page_size < 1 || pages_per_row < 1)) return SI_ERR_INVALID_ARGUMENT;
+  if (rows == 0 || width == 0) return SI_OK;
+  if (!idx || !lens || !out_slots) return SI_ERR_INVALID_ARGUMENT;
+  hipError_t e = launch_gather_slots(idx, rows, width, lens, row_start, page_table,
+                                     page_table ? pages_per_row : 0, page_table ? page_size : 1,
+                                     out_slots, stream);
+  return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
+}
+
 }  // extern "C"

@@ -236,6 +236,14 @@ constexpr int kMaxTopk = 4096;
 hipError_t launch_score_rows_listed(const ScoreArgs& a, const int32_t* row_list,
                                     const int32_t* row_count, hipStream_t st);
 
+hipError_t launch_block_positions(const int32_t* blocks, int32_t n_q, int32_t heads,
+                                  int32_t width, const int64_t* qpos, int64_t n_pos, int32_t bs,
+                                  int32_t* out, int32_t out_width, int32_t* count, hipStream_t st);
+hipError_t launch_gather_slots(const int32_t* idx, int32_t rows, int32_t width,
+                               const int32_t* lens, const int64_t* row_start,
+                               const int32_t* table, int32_t ppr, int32_t page, int64_t* out,
+                               hipStream_t st);
+
 hipError_t launch_witness(int32_t* idx, int32_t rows, int32_t topk, const int32_t* lens,
                           int32_t S, int32_t keep, int32_t B, hipStream_t st);
 

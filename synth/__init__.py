@@ -200,3 +200,53 @@ def witness_rows(seed: int = 0, rows: int = 64, topk: int = 64, max_len: int = 3
         row[oob] = L + g.integers(0, 4 * L + 1, size=int(oob.sum()))
         out[r] = row
     return out, lens
+
+
+def block_lists(seed: int = 0, n_q: int = 4096, H: int = 8, n_pos: int = 131072,
+                block_size: int = 128, top_blocks: int = 32, init_blocks: int = 1,
+                local_blocks: int = 2, query_pos=None, messy: bool = False):
+    """Block lists shaped like a selection: per (query, KV head), the forced first and last
+    blocks plus random others up to the budget, ascending, -1 padded to the selection width.
+    messy: shuffled, with repeats, out-of-range blocks and padding in the middle."""
+    g = _streams(seed, 1)[0]
+    if query_pos is None:
+        stride = n_pos // n_q
+        query_pos = stride * np.arange(n_q, dtype=np.int64) + (stride - 1)
+    query_pos = np.asarray(query_pos, dtype=np.int64)
+    width = max(top_blocks, init_blocks + local_blocks, 1)
+    out = np.full((len(query_pos), H, width), -1, dtype=np.int32)
+    nb_all = -(-n_pos // block_size)
+    for q, p in enumerate(query_pos):
+        n = 0 if p < 0 else min(int(p) // block_size + 1, nb_all)
+        for h in range(H):
+            forced = set(range(min(init_blocks, n))) | set(range(max(0, n - local_blocks), n))
+            budget = max(top_blocks, len(forced))
+            rest = np.setdiff1d(np.arange(n), np.fromiter(forced, int, len(forced)))
+            extra = g.choice(rest, size=min(budget - len(forced), len(rest)), replace=False)
+            sel = np.sort(np.concatenate([np.fromiter(forced, int, len(forced)), extra]))
+            row = np.full(width, -1, dtype=np.int32)
+            row[:len(sel)] = sel
+            if messy:
+                k = int(g.integers(0, width + 1))
+                row[g.integers(0, width, size=k // 2)] = g.integers(-3, nb_all + 4, size=k // 2)
+                row = g.permutation(row)
+            out[q, h] = row
+    return out, query_pos
+
+
+def kv_layout(seed: int, lens, page_size: int = 128, spare_pages: int = 2):
+    """KV placement of ragged rows: flat starts (rows back to back) and a page table
+    of shuffled physical pages (-1 for the spare, unallocated table entries)."""
+    g = _streams(seed, 1)[0]
+    lens = np.asarray(lens, dtype=np.int64)
+    starts = np.zeros(len(lens), dtype=np.int64)
+    starts[1:] = np.cumsum(lens)[:-1]
+    pages = -(-np.maximum(lens, 0) // page_size)
+    ppr = int(pages.max()) + spare_pages if len(lens) else 1
+    phys = g.permutation(int(pages.sum()) + 7).astype(np.int32)
+    table = np.full((len(lens), ppr), -1, dtype=np.int32)
+    at = 0
+    for r, n in enumerate(pages):
+        table[r, :n] = phys[at:at + n]
+        at += n
+    return starts, table

@@ -217,3 +217,43 @@ def test_dosa_refusals(L):
     assert L.dosa_prune_topk(al(q), al(k), 1, _p(w), H, _p(vis), 0, H, D, n_k, K, C.byref(good),
                              _p(out), None, None, _p(ws), 16, None) == OK
     np.testing.assert_array_equal(out, 3)
+
+
+def test_positions_and_gather_refusals(L):
+    blocks = np.zeros(2 * 2 * 4, np.int32)
+    pos = np.zeros(2, np.int64)
+    out = np.full(2 * 2 * 16, 5, np.int32)
+    cnt = np.full(4, 5, np.int32)
+
+    def pcall(n_q=2, H=2, width=4, n_pos=100, bs=4, ow=16, b=_p(blocks), qp=_p(pos)):
+        return L.positions_of_blocks(b, n_q, H, width, qp, n_pos, bs, _p(out), ow, _p(cnt), None)
+
+    assert pcall(bs=0) == INVALID
+    assert pcall(n_q=-1) == INVALID
+    assert pcall(width=4097) == INVALID
+    assert pcall(n_pos=1 << 31) == INVALID
+    assert pcall(ow=15) == INVALID  # 4 blocks of 4 can cover 16 positions
+    assert pcall(b=None) == INVALID
+    assert pcall(qp=None) == INVALID
+    assert pcall(n_q=0) == OK and pcall(H=0) == OK
+    np.testing.assert_array_equal(out, 5)
+    np.testing.assert_array_equal(cnt, 5)
+
+    idx = np.zeros(2 * 8, np.int32)
+    lens = np.zeros(2, np.int32)
+    starts = np.zeros(2, np.int64)
+    table = np.zeros(2 * 3, np.int32)
+    slots = np.full(2 * 8, 7, np.int64)
+
+    def gcall(rows=2, width=8, rs=_p(starts), pt=None, ppr=3, page=4, i=_p(idx)):
+        return L.gather_slots(i, rows, width, _p(lens), rs, pt, ppr, page, _p(slots), None)
+
+    assert gcall(rows=-1) == INVALID
+    assert gcall(width=(1 << 26) + 1) == INVALID
+    assert gcall(rs=None) == INVALID  # neither mapping
+    assert gcall(pt=_p(table)) == INVALID  # both mappings
+    assert gcall(rs=None, pt=_p(table), page=0) == INVALID
+    assert gcall(rs=None, pt=_p(table), ppr=0) == INVALID
+    assert gcall(i=None) == INVALID
+    assert gcall(rows=0) == OK and gcall(width=0) == OK
+    np.testing.assert_array_equal(slots, 7)
