@@ -212,12 +212,48 @@ def bench_indexer(args, cfg, workload):
                            key_dtype={0: "f32", 1: "bf16", 2: "fp8_e4m3fn"}[cfg["k_dtype"]],
                            pairs_per_step=pairs),
                roofline=roof, kernels=kern, event_ms_per_step=step_ms)
+    out["consumer"] = bench_gather(args, cfg, d, out_idx, workload)
     if workload == "decode":
         out["prior_path"] = bench_prior(args, cfg, d, out_idx, wit)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline_rows(cfg, args.cpu_seconds, wit)
     return out
+
+
+def bench_gather(args, cfg, d, idx, workload):
+    """The consumer's gather list of the step's witness-merged rows (not part
+    of the step): decode rows live back to back in a flat KV buffer (row
+    starts = the rows' key offsets); prefill rows share one sequence held in
+    shuffled 128-token pages."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_indexer_02_amd as si
+    import synth
+    n_q, K = idx.shape
+    dev = idx.device
+    kw = {}
+    if workload == "decode":
+        kw["row_start"] = d["k_row_offset"]
+        extra = n_q * 8
+    else:
+        _, table = synth.kv_layout(seed=5, lens=[cfg["n_k"]], page_size=128)
+        kw["page_table"] = torch.from_numpy(np.repeat(table, n_q, axis=0)).to(dev)
+        kw["page_size"] = 128
+        extra = n_q * table.size * 4  # every row's copy of the sequence's table
+    out = torch.empty((n_q, K), dtype=torch.int64, device=dev)
+
+    def gather():
+        si.gather_slots(idx, d["vis_len"], out=out, **kw)
+
+    _, per = timed_steps([("gather", gather)], args.steps, args.warmup)
+    nbytes = n_q * K * (4 + 8) + n_q * 4 + extra
+    return dict(gather_slots=dict(ms=per["gather"], algo_bytes=nbytes,
+                                  gbs=nbytes / per["gather"] / 1e6,
+                                  hbm_frac=nbytes / per["gather"] / 1e6 / PEAK_HBM_GBS,
+                                  layout="flat row starts" if workload == "decode"
+                                  else "paged, 128-token pages"))
 
 
 PRIOR_EPS = 0.3  # query perturbation standing in for the previous decode step
@@ -308,6 +344,17 @@ def bench_block(args):
                                out_width=width, out_blocks=out, out_count=cnt, workspace=ws)
 
     wall_ms, per = timed_steps([("select", step)], args.steps, args.warmup)
+    # the consumer's positions of the selection (not part of the step)
+    ow = width * bs
+    cov = torch.empty((cfg["n_q"], H, ow), dtype=torch.int32, device=dev)
+    cov_n = torch.empty((cfg["n_q"], H), dtype=torch.int32, device=dev)
+
+    def positions():
+        si.positions_of_blocks(out, pos, cfg["n_pos"], bs, out_width=ow, out_pos=cov,
+                               out_count=cov_n)
+
+    _, pp = timed_steps([("positions", positions)], args.steps, args.warmup)
+    pbytes = cfg["n_q"] * H * (width * 4 + ow * 4 + 4) + cfg["n_q"] * 8
     pos_np = np.minimum(cfg["query_pos"], cfg["n_pos"] - 1)
     dots = int((pos_np + 1).sum()) * H  # (query, head, visible position) dots
     ops = dots * 2.0 * D
@@ -322,7 +369,11 @@ def bench_block(args):
                  roofline=dict(bound="alu", achieved=ach, peak=PEAK_VALU_TOPS, unit="TFLOP/s",
                                frac=ach / PEAK_VALU_TOPS,
                                traffic=counters_for("block"),
-                               kernel="block_max128"))
+                               kernel="block_max128"),
+                 consumer=dict(positions_of_blocks=dict(
+                     ms=pp["positions"], algo_bytes=pbytes, gbs=pbytes / pp["positions"] / 1e6,
+                     hbm_frac=pbytes / pp["positions"] / 1e6 / PEAK_HBM_GBS,
+                     out_width=ow)))
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         n = 4

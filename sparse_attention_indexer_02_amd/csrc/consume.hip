@@ -3,8 +3,9 @@
 //
 //  * block_positions: the positions a block list covers (ferrox-core
 //    block_sparse.rs, positions_of_blocks): ascending, deduplicated, and
-//    clipped to the keys that exist and to the query's own position.  One
-//    256-thread workgroup per (query, KV head) list.  A list's entries
+//    clipped to the keys that exist and to the query's own position.  Lists
+//    of at most 64 entries take one wave each (block_positions_wave, below);
+//    longer ones one 256-thread workgroup each.  A list's entries
 //    become 64-bit keys, larger for lower blocks and 0 for entries that
 //    cover nothing (padding, blocks past the query or the keys); a list that
 //    is not already in descending key order (block_sparse_select's are) is
@@ -83,12 +84,142 @@ __global__ __launch_bounds__(kPosThreads) void block_positions(
   if (t == 0 && count) count[l] = total;
 }
 
+// Lists of at most 64 entries: one wave per list, four per workgroup, no
+// barriers.  Lane j holds entry j; an unordered list is bitonic-sorted
+// across the lanes; a wave scan gives the offsets; each lane writes four
+// consecutive slots per 1 KB wave store (as one 16-byte store when rows are
+// 16-byte aligned), finding the first slot's block by a binary search and
+// the next three by stepping.
+constexpr int kPosWaveLists = 4;
+
+__device__ __forceinline__ uint64_t join_u64(uint32_t lo, uint32_t hi) {
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  return join_u64(__shfl_xor((uint32_t)v, m), __shfl_xor((uint32_t)(v >> 32), m));
+}
+// lane + 1's value (lane 63: its own)
+__device__ __forceinline__ uint64_t shfl_next_u64(uint64_t v) {
+  return join_u64(__shfl_down((uint32_t)v, 1), __shfl_down((uint32_t)(v >> 32), 1));
+}
+// lane - 1's value (lane 0: its own)
+__device__ __forceinline__ uint64_t shfl_prev_u64(uint64_t v) {
+  return join_u64(__shfl_up((uint32_t)v, 1), __shfl_up((uint32_t)(v >> 32), 1));
+}
+
+__global__ __launch_bounds__(64 * kPosWaveLists) void block_positions_wave(
+    const int32_t* __restrict__ blocks, int width, int heads, int64_t lists,
+    const int64_t* __restrict__ qpos, int64_t n_pos, int bs, int32_t* __restrict__ out,
+    int64_t out_width, bool vec4, int32_t* __restrict__ count) {
+  __shared__ int offw[kPosWaveLists][64];
+  __shared__ int startw[kPosWaveLists][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t l = (int64_t)blockIdx.x * kPosWaveLists + wv;
+  if (l >= lists) return;
+  const int32_t b = lane < width ? blocks[l * width + lane] : -1;
+  const int64_t qp = qpos[l / heads];
+  const int64_t lim = qp < 0 ? 0 : (qp + 1 < n_pos ? qp + 1 : n_pos);
+  const int64_t nbv = (lim + bs - 1) / bs;
+  uint64_t key = (b >= 0 && b < nbv) ? ((1ull << 32) | (uint64_t)(~(uint32_t)b)) : 0ull;
+  // descending keys = ascending blocks, entries covering nothing last
+  if (__any(lane < 63 && key < shfl_next_u64(key))) {
+    for (int size = 2; size <= 64; size <<= 1)
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        const uint64_t other = shfl_xor_u64(key, stride);
+        const bool desc = (lane & size) == 0, lower = (lane & stride) == 0;
+        const uint64_t mx = key > other ? key : other, mn = key > other ? other : key;
+        key = (lower == desc) ? mx : mn;
+      }
+  }
+  const uint64_t prev = shfl_prev_u64(key);
+  const bool keep = key != 0ull && (lane == 0 || prev != key);
+  const int start = (int)((int64_t)(~(uint32_t)key) * bs);  // < lim when kept
+  int len = 0;
+  if (keep) {
+    const int64_t end = (int64_t)start + bs < lim ? (int64_t)start + bs : lim;
+    len = (int)(end - start);
+  }
+  const int incl = wave_incl_scan(len);
+  const int total = __shfl(incl, 63);
+  offw[wv][lane] = incl - len;
+  startw[wv][lane] = start;
+  __builtin_amdgcn_wave_barrier();
+  const int* off = offw[wv];
+  const int* st = startw[wv];
+  int32_t* o = out + l * out_width;
+  // a list of whole blocks with no repeats (a selection's, but for its
+  // clipped last block): slot s lies in kept entry s / bs
+  const uint64_t kept = __ballot(keep);
+  const int nk = __popcll(kept);
+  const bool whole = kept == (nk == 64 ? ~0ull : ((1ull << nk) - 1ull)) &&
+                     !__any(keep && lane != nk - 1 && len != bs);
+#pragma unroll 4
+  for (int64_t base = 4 * lane; base < out_width; base += 256) {
+    int32_t v[4];
+    if (whole && (bs & 3) == 0) {
+      // the four slots share a block
+      const uint32_t s = (uint32_t)base;
+      const uint32_t q = s / (uint32_t)bs, e = q < 63u ? q : 63u;
+      const int32_t v0 = st[e] + (int32_t)(s - e * (uint32_t)bs);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = s + j < (uint32_t)total ? v0 + j : -1;
+    } else if (whole) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t s = (uint32_t)(base + j);
+        const uint32_t q = s / (uint32_t)bs, e = q < 63u ? q : 63u;
+        v[j] = s < (uint32_t)total ? st[e] + (int32_t)(s - e * (uint32_t)bs) : -1;
+      }
+    }
+    int e = 0;
+    if (!whole && base < total) {
+      int lo = 0, hi = 63;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= base) lo = mid; else hi = mid - 1;
+      }
+      e = lo;
+    }
+    if (!whole) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t s = base + j;
+        if (s < total) {
+          while (e < 63 && off[e + 1] <= s) ++e;
+          v[j] = st[e] + (int32_t)(s - off[e]);
+        } else {
+          v[j] = -1;
+        }
+      }
+    }
+    if (vec4) {
+      // streamed out: the consumer reads it, this kernel never does
+      typedef int i32x4 __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(i32x4{v[0], v[1], v[2], v[3]},
+                                  reinterpret_cast<i32x4*>(o + base));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (base + j < out_width) o[base + j] = v[j];
+    }
+  }
+  if (lane == 0 && count) count[l] = total;
+}
+
 hipError_t launch_block_positions(const int32_t* blocks, int32_t n_q, int32_t heads,
                                   int32_t width, const int64_t* qpos, int64_t n_pos, int32_t bs,
                                   int32_t* out, int32_t out_width, int32_t* count,
                                   hipStream_t st) {
   const int64_t lists = (int64_t)n_q * heads;
   if (lists == 0) return hipSuccess;
+  if (width <= 64) {
+    const bool vec4 = out_width % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+    hipLaunchKernelGGL(block_positions_wave,
+                       dim3((unsigned)((lists + kPosWaveLists - 1) / kPosWaveLists)),
+                       dim3(64 * kPosWaveLists), 0, st, blocks, width, heads, lists, qpos, n_pos,
+                       bs, out, (int64_t)out_width, vec4, count);
+    return hipGetLastError();
+  }
   const int P = next_pow2(width > 1 ? width : 1);
   const size_t lds = (size_t)P * (sizeof(uint64_t) + sizeof(int));
   hipLaunchKernelGGL(block_positions, dim3((unsigned)lists), dim3(kPosThreads), lds, st, blocks,
