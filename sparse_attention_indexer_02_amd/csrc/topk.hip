@@ -3,8 +3,9 @@
 // reproducible; the final selection is by full score).
 //
 // Kernels:
-//  * topk_block: rows of at most 8192 scores, K <= 2048, one workgroup per
-//    row holding the row in registers (steps in topk_block.hpp).  Longer
+//  * topk_block: rows of at most 8192 scores, K <= 2048, one 512-thread
+//    workgroup per row holding the row in registers (steps in
+//    topk_block.hpp).  Longer
 //    rows (K <= 2048, with a workspace) are cut into 8192-score chunks whose
 //    ordered top-K lists, with the chunks' position maps, are selected from
 //    again by the same kernel until one chunk remains (topk_next_len gives
@@ -91,7 +92,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kBT) void topk_block(TopkArgs a) {
+// eight waves per SIMD (64 VGPRs): four rows' 32 waves fill a CU
+__global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(8))) void topk_block(
+    TopkArgs a) {
   __shared__ TopkSmem S;
   int r = (int)blockIdx.x;
   if (a.row_list) {

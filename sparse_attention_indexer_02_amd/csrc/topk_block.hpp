@@ -1,4 +1,4 @@
-// Per-row top-K with one 256-thread workgroup and the row in registers,
+// Per-row top-K with one 512-thread workgroup and the row in registers,
 // for rows of at most 8192 scores and K <= 2048 (the block kernel of the
 // top-K stage and its chunk passes).
 #pragma once
@@ -8,11 +8,14 @@
 namespace si {
 
 // ---------------------------------------------------------------------------
-// Rows of at most 8192 scores, K <= 2048: one 256-thread workgroup per row.
-// Thread t holds the float4 groups t, t + 256, ..., t + 1792 of the row
-// (positions 4 t + 1024 j + c), so each load instruction of the workgroup
-// reads 4 KB contiguous and a row of n scores keeps all four waves busy on
-// its first ceil(n / 1024) group rows (the rest are skipped uniformly).
+// Rows of at most 8192 scores, K <= 2048: one 512-thread workgroup per row,
+// 16 scores per thread (eight waves per row: with four rows per CU, limited
+// by LDS, the CU holds its full 32 waves, and more waves per row measured
+// faster than more registers per thread).  Thread t holds the float4 groups
+// t, t + 512, t + 1024, t + 1536 of the row (positions 4 t + 2048 j + c),
+// so the workgroup's four loads of group row j read 8 KB contiguous, and a
+// row of n scores keeps all eight waves busy on its first ceil(n / 2048)
+// group rows (the rest are skipped uniformly).
 //  A. load (a NaN score is taken as -inf) and the row's value range;
 //  B. histogram over 4096 bins linear in score value over [vmin, vmax];
 //  C. scan from the top bin: the bin b1 holding the K-th item, and per bin
@@ -32,8 +35,8 @@ namespace si {
 // (8191 - position); composites compare as (score desc, index asc), and the
 // bin rides along so the rank step need not recompute it.
 // ---------------------------------------------------------------------------
-constexpr int kBT = 256;              // threads per row
-constexpr int kBPer = 32;             // positions per thread
+constexpr int kBT = 512;              // threads per row
+constexpr int kBPer = 16;             // positions per thread
 constexpr int kBN = kBT * kBPer;      // 8192
 static_assert(kBN == kBlockTopkMaxN, "block top-K row capacity");
 constexpr int kBGroups = kBPer / 4;   // float4 groups per thread
@@ -103,7 +106,7 @@ struct TopkSmem {
   int lcount;
 };
 
-// One row (or one chunk of a row) with the 256 threads of the calling
+// One row (or one chunk of a row) with the kBT threads of the calling
 // workgroup; every thread must call it (it synchronises the workgroup).
 __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy, TopkSmem& S) {
   BlockSmem& sm = S.sm;
@@ -393,12 +396,13 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
 #pragma unroll
       for (int j = 0; j < kBGroups; ++j) {
         const uint32_t g4 = (eqm >> (4 * j)) & 0xFu;
-        if (g4) atomicOr(&sm.x.eq.bits[(t >> 3) + 32 * j], g4 << (4 * (t & 7)));
+        if (g4) atomicOr(&sm.x.eq.bits[(t >> 3) + (kBStep / 32) * j], g4 << (4 * (t & 7)));
       }
       __syncthreads();
       int tot;
-      const uint32_t wbits = sm.x.eq.bits[t];  // kBN / 32 == kBT words
-      sm.x.eq.pre[t] = (uint32_t)block_excl_scan<kBT>(__builtin_popcount(wbits), red, &tot);
+      const uint32_t wbits = t < kBN / 32 ? sm.x.eq.bits[t] : 0u;
+      const int wp = block_excl_scan<kBT>(__builtin_popcount(wbits), red, &tot);
+      if (t < kBN / 32) sm.x.eq.pre[t] = (uint32_t)wp;
       __syncthreads();
       uint32_t keep = 0u;
 #pragma unroll
