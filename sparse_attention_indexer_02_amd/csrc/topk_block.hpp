@@ -102,7 +102,7 @@ struct TopkSmem {
   BlockSmem sm;
   int red[kBT / 64 + 8];
   float fred[2][kBT / 64];
-  uint32_t wred[kBT / 64];
+  uint32_t crowd;  // largest selected count of a bin
   int lcount;
 };
 
@@ -112,7 +112,6 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   BlockSmem& sm = S.sm;
   int* red = S.red;
   float (*fred)[kBT / 64] = S.fred;
-  uint32_t* wred = S.wred;
   int& lcount = S.lcount;
   const int t = (int)threadIdx.x;
   const int lane = t & 63, wid = t >> 6;
@@ -169,7 +168,10 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
 #pragma unroll
   for (int k = 0; k < kBins / (4 * kBT); ++k)
     *reinterpret_cast<uint4*>(&sm.bins[4 * t + 4 * kBT * k]) = make_uint4(0u, 0u, 0u, 0u);
-  if (t == 0) lcount = 0;
+  if (t == 0) {
+    lcount = 0;
+    S.crowd = 0u;
+  }
   // (adding +0 also turns -0 into +0, so the keys below need no fold)
   auto clean = [](float v) { return v == v ? v + 0.0f : -__builtin_inff(); };
   auto key_of = [](float v) {  // order_key for a value that is not -0
@@ -298,12 +300,10 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
       *reinterpret_cast<uint4*>(&sm.bins[top - 3 - 4 * v]) =
           make_uint4(c[4 * v + 3], c[4 * v + 2], c[4 * v + 1], c[4 * v + 0]);
     crowd = __ockl_wfred_max_u32(crowd);
-    if (lane == 0) wred[wid] = crowd;
+    if (lane == 0) atomicMax(&S.crowd, crowd);
   }
   __syncthreads();
-  uint32_t crowd = 0u;
-#pragma unroll
-  for (int i = 0; i < kBT / 64; ++i) crowd = wred[i] > crowd ? wred[i] : crowd;
+  const uint32_t crowd = S.crowd;
 
   // D. the exact threshold value T inside b1
   float thr = 0.0f;
