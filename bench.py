@@ -425,13 +425,13 @@ def bench_dosa(args):
                        device=dev)
     stats = {}
 
-    def dosa():
+    def dosa(shared=False):
         _, _, st = si.dosa_prune_topk(d["q"], d["k"], d["w"], d["vis_len"], K,
                                       n_seeds=dp["n_seeds"], n_rep_queries=dp["n_rep_queries"],
                                       rep_topk=dp["rep_topk"], kept_heads=dp["kept_heads"],
                                       neg_active_frac=dp["neg_active_frac"],
                                       survivor_capacity=cap, out_idx=out_i, out_score=out_s,
-                                      want_stats=True, workspace=ws)
+                                      want_stats=True, workspace=ws, shared_streams=shared)
         stats.update(st)
 
     def unpruned():
@@ -439,6 +439,14 @@ def bench_dosa(args):
                           out_score=ref_s, workspace=ws_u)
 
     pairs = int(cfg["vis_len"].astype(np.int64).sum())
+    # 4-query shared streams: the same result, timed first so that the
+    # per-row run's outputs and stats are the ones checked below
+    unpruned()
+    _, per_g = timed_steps([("groups", lambda: dosa(True))], args.steps, args.warmup)
+    torch.cuda.synchronize()
+    eq_g = bool(torch.equal(out_i, ref_i) and torch.equal(out_s.view(torch.int32),
+                                                          ref_s.view(torch.int32)))
+    shared_n = int(stats["n_shared"].sum().item())
     wall_ms, per = timed_steps([("dosa", dosa)], args.steps, args.warmup)
     _, per_u = timed_steps([("unpruned", unpruned)], args.steps, args.warmup)
     torch.cuda.synchronize()
@@ -471,7 +479,9 @@ def bench_dosa(args):
                          bit_identical_to_unpruned=equal,
                          survival=float(surv.clip(0).sum()) / max(scanned, 1),
                          fallback_rows=int(fb.sum()), head_dots=head_dots,
-                         dense_head_dots=pairs * H))
+                         dense_head_dots=pairs * H,
+                         shared_streams=dict(ms=per_g["groups"], survivors_shared=shared_n,
+                                             bit_identical_to_unpruned=eq_g)))
     return out
 
 

@@ -204,12 +204,25 @@ size_t rows_topk_workspace(int32_t n_rows, int64_t max_vis, int32_t topk);
  *                            would use).
  *  params->survivor_capacity survivors a row may keep (1..8192); a row with
  *                            more takes the exact unpruned path.
+ *  params->shared_streams    0: one survivor stream per row.  1: the
+ *                            section-4 compaction variant: rows in groups
+ *                            of 4 (rows 4g..4g+3); keys passing the bound
+ *                            for at least 2 of a group's rows and inside
+ *                            its common visible prefix form the group's
+ *                            shared stream, rescored once per key tile for
+ *                            all 4 rows; the rest go to per-row solo
+ *                            streams.  Rows over survivor_capacity take the
+ *                            exact path, as with per-row streams, and no
+ *                            part in their group's split.  The result is
+ *                            the same either way.
  * The workspace (dosa_prune_topk_workspace) holds the seed scores
  * [n_q, n_seeds], survivor lists [n_q, capacity] and, for the exact path,
  * full score rows [n_q, n_k] (f32).
  *  stats (optional, device pointers, each may be NULL): tau [n_q],
  *        n_survivors [n_q] (keys passing the bound), fallback [n_q] (1 when
- *        the row took the exact path).
+ *        the row took the exact path), n_shared [n_q] (those of the row's
+ *        survivors its group's shared stream carries; 0 without shared
+ *        streams).
  * Rows fall back to the exact path as a whole when fewer than n_seeds keys
  * are visible to every row.
  * Errors: as idx_score_topk, plus INVALID_ARGUMENT for params out of range
@@ -223,12 +236,14 @@ typedef struct {
   float neg_active_frac;
   const int32_t* seed_ids;
   int32_t survivor_capacity;
+  int32_t shared_streams;
 } si_dosa_params;
 
 typedef struct {
   float* tau;
   int32_t* n_survivors;
   int32_t* fallback;
+  int32_t* n_shared;
 } si_dosa_stats;
 
 si_status dosa_prune_topk(const void* q, const void* k, si_dtype dtype, const float* w,

@@ -31,11 +31,13 @@ class SparseIndexerError(RuntimeError):
 class DosaParams(C.Structure):
     _fields_ = [("n_seeds", C.c_int32), ("n_rep_queries", C.c_int32), ("rep_topk", C.c_int32),
                 ("kept_heads", C.c_int32), ("neg_active_frac", C.c_float),
-                ("seed_ids", C.c_void_p), ("survivor_capacity", C.c_int32)]
+                ("seed_ids", C.c_void_p), ("survivor_capacity", C.c_int32),
+                ("shared_streams", C.c_int32)]
 
 
 class DosaStats(C.Structure):
-    _fields_ = [("tau", C.c_void_p), ("n_survivors", C.c_void_p), ("fallback", C.c_void_p)]
+    _fields_ = [("tau", C.c_void_p), ("n_survivors", C.c_void_p), ("fallback", C.c_void_p),
+                ("n_shared", C.c_void_p)]
 
 
 _lib = None
@@ -251,7 +253,7 @@ def rows_topk(scores, vis_len, topk, *, k_row_offset=None, n_k=None, max_vis=Non
 def dosa_prune_topk(q, k, w, vis_len, topk, *, n_seeds=12288, n_rep_queries=4, rep_topk=2048,
                     kept_heads=16, neg_active_frac=0.5, seed_ids=None, survivor_capacity=None,
                     out_idx=None, out_score=None, want_scores=True, want_stats=False,
-                    workspace=None):
+                    workspace=None, shared_streams=False):
     """DoSA certified-prune top-K (bit-identical to idx_score_topk); returns
     (idx, scores|None, stats dict|None)."""
     _dev_tensor(q, "q", torch.bfloat16)
@@ -265,7 +267,7 @@ def dosa_prune_topk(q, k, w, vis_len, topk, *, n_seeds=12288, n_rep_queries=4, r
         survivor_capacity = max(4 * topk, 8192)
     w_stride = H if w.dim() == 2 else 0
     p = DosaParams(n_seeds, n_rep_queries, rep_topk, kept_heads, neg_active_frac,
-                   _ptr(seed_ids), survivor_capacity)
+                   _ptr(seed_ids), survivor_capacity, 1 if shared_streams else 0)
     if out_idx is None:
         out_idx = torch.empty((n_q, topk), dtype=torch.int32, device=dev)
     if out_score is None and want_scores:
@@ -275,8 +277,10 @@ def dosa_prune_topk(q, k, w, vis_len, topk, *, n_seeds=12288, n_rep_queries=4, r
     if want_stats:
         stats = dict(tau=torch.empty(n_q, dtype=torch.float32, device=dev),
                      n_survivors=torch.empty(n_q, dtype=torch.int32, device=dev),
-                     fallback=torch.empty(n_q, dtype=torch.int32, device=dev))
-        sp = DosaStats(_ptr(stats["tau"]), _ptr(stats["n_survivors"]), _ptr(stats["fallback"]))
+                     fallback=torch.empty(n_q, dtype=torch.int32, device=dev),
+                     n_shared=torch.empty(n_q, dtype=torch.int32, device=dev))
+        sp = DosaStats(_ptr(stats["tau"]), _ptr(stats["n_survivors"]), _ptr(stats["fallback"]),
+                       _ptr(stats["n_shared"]))
     need = lib().dosa_prune_topk_workspace(n_q, H, D, n_k, topk, C.byref(p))
     ws, ws_bytes = _workspace(need, dev, workspace)
     st = lib().dosa_prune_topk(_ptr(q), _ptr(k), SI_BF16, _ptr(w), w_stride, _ptr(vis_len), n_q, H,

@@ -29,7 +29,17 @@
 //               at least the score this device computes.
 //   compact     ballot bitmap -> ascending survivor ids; more than
 //               survivor_capacity sends the row to the exact path.
-//   rescore     survivors with the shared micro-kernel; keep s >= tau.
+//               With shared streams (section 4's compaction variant): rows
+//               go in groups of 4; a key that survives for at least 2 of
+//               the group's rows and lies in the group's common visible
+//               prefix goes to the group's shared stream, every other
+//               survivor to its row's solo stream (rows over the capacity
+//               take the exact path and no part in the split).
+//   rescore     survivors with the shared micro-kernel; keep s >= tau.  A
+//               shared stream's key tile is fetched once into LDS and scored
+//               for all 4 rows (one wave per row); a row keeps a shared key
+//               iff its own s >= tau (a key whose bound failed for the row
+//               has s <= U < tau, so this adds nothing wrong).
 //   merge       seed top-K (sorted) merged with the sorted kept survivors;
 //               first K by (score desc, key asc).
 //   fallback    listed rows (overflow, or every row when c < n_seeds or a
@@ -53,8 +63,8 @@ struct DosaCtx {
 struct DosaLayout {
   size_t ctx, rep_q, rep_w, rep_vis, rep_scores, rep_ids, counts, seeds, seed_mask, seed_keys,
       seed_scores, stat_cnt, stat_sum, top_idx, top_score, plan_a, plan_w, plan_c, knorm, bitmap,
-      surv_ids, surv_cnt, row_fb, kept_score, kept_id, kept_cnt, fb_list, fb_scores, topk_ws,
-      topk_ws_bytes, total;
+      surv_ids, surv_cnt, row_fb, kept_score, kept_id, kept_cnt, fb_list, fb_scores, shared_ids,
+      shared_cnt, solo_cnt, shared_n, topk_ws, topk_ws_bytes, total;
 };
 
 static size_t au(size_t x) { return (x + 255) / 256 * 256; }
@@ -99,6 +109,14 @@ static DosaLayout dosa_layout(int32_t n_q, int32_t H, int32_t D, int64_t n_k, in
   L.kept_cnt = take(nq * 4);
   L.fb_list = take(nq * 4);
   L.fb_scores = take(nq * nk * 4);
+  // 4-query groups: shared streams [groups, 2 cap], their lengths, each
+  // row's solo stream length and its survivors taken through the shared
+  // stream
+  const size_t ng = (nq + 3) / 4;
+  L.shared_ids = take(ng * 2 * cap * 4);
+  L.shared_cnt = take(ng * 4);
+  L.solo_cnt = take(nq * 4);
+  L.shared_n = take(nq * 4);
   // candidate lists of the chunked top-K, shared by its three uses (the
   // representative rows, the seed rows and the exact-path rows run one
   // after the other)
@@ -714,19 +732,29 @@ __global__ __launch_bounds__(kCompThreads) void dosa_compact(
   }
 }
 
+// Slot of this lane's item in a list whose length is *cnt, for the lanes
+// with keep set: one atomic per wave (every lane of the wave calls it).
+__device__ __forceinline__ int wave_append(bool keep, int32_t* cnt) {
+  const uint64_t m = __ballot(keep);
+  int base = 0;
+  if ((threadIdx.x & 63) == 0 && m) base = atomicAdd(cnt, __popcll(m));
+  base = __shfl(base, 0);
+  return base + __popcll(m & ((1ull << (threadIdx.x & 63)) - 1ull));
+}
+
 // Exact rescoring of survivors with the shared micro-kernel (keys gathered
 // straight into the k-step layout).  One workgroup per row.
 template <int MT, int KS>
 __global__ __launch_bounds__(256) void dosa_rescore(
     const DosaCtx* ctx, const uint16_t* __restrict__ q, const float* __restrict__ w,
     int64_t w_stride, int H, const uint16_t* __restrict__ k, const float* __restrict__ top_score,
-    int topk, const int32_t* __restrict__ surv_ids, const int32_t* __restrict__ surv_cnt,
+    int topk, const int32_t* __restrict__ surv_ids, const int32_t* __restrict__ list_cnt,
     const int32_t* __restrict__ row_fb, int cap, float* __restrict__ kept_score,
     int32_t* __restrict__ kept_id, int32_t* __restrict__ kept_cnt) {
   constexpr int D = 16 * KS;
   const int r = blockIdx.x;
   if (ctx->global_fallback || row_fb[r]) return;
-  const int n = surv_cnt[r];
+  const int n = list_cnt[r];
   if (n == 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float tau = top_score[(int64_t)r * topk + topk - 1];
@@ -747,16 +775,217 @@ __global__ __launch_bounds__(256) void dosa_rescore(
         },
         acc);
     float s = head_reduce<MT>(acc[0], wv);
-    if (lane < 32 && in && s >= tau) {
-      int slot = atomicAdd(&kept_cnt[r], 1);
+    const bool keep = lane < 32 && in && s >= tau;
+    const int slot = wave_append(keep, &kept_cnt[r]);
+    if (keep) {
       kept_score[(int64_t)r * cap + slot] = s;
       kept_id[(int64_t)r * cap + slot] = id;
     }
   }
 }
 
+// 4-query groups (one workgroup per group).  A row whose survivors (keys
+// passing its bound) exceed the capacity takes the exact path, as with
+// per-row streams, and its bits take no part in the split.  Of the other
+// rows' survivors, a key set for at least 2 of them and below the group's
+// common visible prefix goes to the shared stream, every other one to its
+// row's solo stream, both ascending.  A shared key is set for at least two
+// rows of at most the capacity each, so the shared stream holds at most
+// 2 * capacity keys, and a row keeps at most its own survivors.  surv_cnt
+// keeps each row's survivor count, shared_n the part the shared stream
+// carries.
+constexpr int kGroupRows = 4;
+__global__ __launch_bounds__(kCompThreads) void dosa_compact_groups(
+    const DosaCtx* ctx, const uint32_t* __restrict__ bitmap, int64_t words,
+    const int32_t* __restrict__ vis_len, int n_q, int64_t n_k, int cap,
+    int32_t* __restrict__ shared_ids, int32_t* __restrict__ shared_cnt,
+    int32_t* __restrict__ surv_ids, int32_t* __restrict__ solo_cnt,
+    int32_t* __restrict__ surv_cnt, int32_t* __restrict__ shared_n, int32_t* __restrict__ row_fb) {
+  __shared__ int red[kCompThreads / 64 + 4];
+  const int g = blockIdx.x, t = threadIdx.x;
+  const int r0 = g * kGroupRows;
+  const int nr = n_q - r0 < kGroupRows ? n_q - r0 : kGroupRows;
+  if (ctx->global_fallback) {
+    if (t < nr) {
+      surv_cnt[r0 + t] = 0;
+      solo_cnt[r0 + t] = 0;
+      shared_n[r0 + t] = 0;
+      row_fb[r0 + t] = 1;
+    }
+    if (t == 0) shared_cnt[g] = 0;
+    return;
+  }
+  int64_t nwr[kGroupRows];
+  int64_t cg = INT64_MAX, nw = 0;
+#pragma unroll
+  for (int i = 0; i < kGroupRows; ++i) {
+    int64_t off, v = 0;
+    if (i < nr) v = visible_len(vis_len, nullptr, r0 + i, n_k, n_k, &off);
+    nwr[i] = (v + 31) / 32;
+    if (i < nr) cg = v < cg ? v : cg;
+    nw = nwr[i] > nw ? nwr[i] : nw;
+  }
+  const int64_t per = (nw + kCompThreads - 1) / kCompThreads;
+  const int64_t w0 = (int64_t)t * per;
+  // each row's survivors
+  int tot[kGroupRows] = {0, 0, 0, 0}, tot_total[kGroupRows];
+  for (int64_t wi = w0; wi < w0 + per && wi < nw; ++wi)
+#pragma unroll
+    for (int i = 0; i < kGroupRows; ++i)
+      if (wi < nwr[i]) tot[i] += __popc(bitmap[(int64_t)(r0 + i) * words + wi]);
+  bool over[kGroupRows];
+#pragma unroll
+  for (int i = 0; i < kGroupRows; ++i) {
+    (void)block_excl_scan<kCompThreads>(tot[i], red, &tot_total[i]);
+    over[i] = tot_total[i] > cap;
+  }
+  // the word's masks (rows taking the exact path contribute none), and the
+  // shared part
+  auto masks = [&](int64_t wi, uint32_t (&m)[kGroupRows]) -> uint32_t {
+#pragma unroll
+    for (int i = 0; i < kGroupRows; ++i)
+      m[i] = (!over[i] && wi < nwr[i]) ? bitmap[(int64_t)(r0 + i) * words + wi] : 0u;
+    const uint32_t two = (m[0] & m[1]) | (m[0] & m[2]) | (m[0] & m[3]) | (m[1] & m[2]) |
+                         (m[1] & m[3]) | (m[2] & m[3]);
+    const int64_t lo = wi * 32;
+    const uint32_t common = lo + 32 <= cg ? 0xFFFFFFFFu
+                            : (lo >= cg ? 0u : ((1u << (uint32_t)(cg - lo)) - 1u));
+    return two & common;
+  };
+  int sh = 0, so[kGroupRows] = {0, 0, 0, 0};
+  for (int64_t wi = w0; wi < w0 + per && wi < nw; ++wi) {
+    uint32_t m[kGroupRows];
+    const uint32_t sm = masks(wi, m);
+    sh += __popc(sm);
+#pragma unroll
+    for (int i = 0; i < kGroupRows; ++i) so[i] += __popc(m[i] & ~sm);
+  }
+  int sh_total, so_total[kGroupRows], spos[kGroupRows];
+  int pos = block_excl_scan<kCompThreads>(sh, red, &sh_total);
+#pragma unroll
+  for (int i = 0; i < kGroupRows; ++i) spos[i] = block_excl_scan<kCompThreads>(so[i], red, &so_total[i]);
+  for (int64_t wi = w0; wi < w0 + per && wi < nw; ++wi) {
+    uint32_t m[kGroupRows];
+    const uint32_t sm = masks(wi, m);
+    for (uint32_t b = sm; b; b &= b - 1)
+      shared_ids[(int64_t)g * 2 * cap + pos++] = (int32_t)(wi * 32 + __ffs(b) - 1);
+#pragma unroll
+    for (int i = 0; i < kGroupRows; ++i)
+      for (uint32_t b = m[i] & ~sm; b; b &= b - 1)
+        surv_ids[(int64_t)(r0 + i) * cap + spos[i]++] = (int32_t)(wi * 32 + __ffs(b) - 1);
+  }
+  if (t == 0) shared_cnt[g] = sh_total;
+  if (t < nr) {
+    surv_cnt[r0 + t] = tot_total[t];
+    solo_cnt[r0 + t] = over[t] ? 0 : so_total[t];
+    shared_n[r0 + t] = over[t] ? 0 : tot_total[t] - so_total[t];
+    row_fb[r0 + t] = over[t] ? 1 : 0;
+  }
+}
+
+// A group's shared stream: each 32-key tile is staged once in LDS (rows
+// padded to 2 D + 16 bytes, so the k-step reads of 32 keys hit distinct
+// banks) and scored by the group's four waves, one per row, with the shared
+// micro-kernel; a row keeps the keys with s >= its tau.  Two LDS tiles
+// alternate: the next tile's keys are loaded into registers during this
+// tile's MFMAs (their ids one tile earlier still) and stored into the other
+// tile, whose last reads the previous iteration's barrier has retired.
+// Grid (groups, kSharedSplit): workgroup (g, y) takes the y-th run of the
+// stream's 32-key tiles, so a long stream spreads over several CUs.
+constexpr int kSharedSplit = 16;
+template <int MT, int KS>
+__global__ __launch_bounds__(256) void dosa_rescore_shared(
+    const DosaCtx* ctx, const uint16_t* __restrict__ q, const float* __restrict__ w,
+    int64_t w_stride, int n_q, int H, const uint16_t* __restrict__ k,
+    const float* __restrict__ top_score, int topk, const int32_t* __restrict__ shared_ids,
+    const int32_t* __restrict__ shared_cnt, const int32_t* __restrict__ row_fb, int cap,
+    float* __restrict__ kept_score, int32_t* __restrict__ kept_id,
+    int32_t* __restrict__ kept_cnt) {
+  constexpr int D = 16 * KS;
+  constexpr int RB = 2 * D + 16;           // LDS bytes per staged key
+  constexpr int CPK = D / 8;               // 16-byte chunks per key
+  constexpr int NC = (32 * CPK + 255) / 256;  // chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) unsigned char tile[2][32 * RB];
+  const int g = blockIdx.x;
+  if (ctx->global_fallback) return;
+  const int n_all = shared_cnt[g];
+  const int tiles = (n_all + 31) / 32;
+  const int tpp = (tiles + kSharedSplit - 1) / kSharedSplit;
+  const int first = (int)blockIdx.y * tpp * 32;
+  if (first >= n_all) return;
+  const int n = n_all - first < tpp * 32 ? n_all - first : tpp * 32;  // keys of this run
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = g * kGroupRows + wave;
+  const bool active = r < n_q && !row_fb[r];
+  const int rq = r < n_q ? r : n_q - 1;
+  const int32_t* ids = shared_ids + (int64_t)g * 2 * cap + first;
+  auto fetch_ids = [&](int t0, int (&id)[NC]) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int c = threadIdx.x + 256 * j;
+      const int i = t0 + c / CPK;
+      id[j] = (c < 32 * CPK && i < n) ? ids[i] : -1;
+    }
+  };
+  auto fetch_keys = [&](const int (&id)[NC], u32x4 (&v)[NC]) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int c = threadIdx.x + 256 * j;
+      v[j] = id[j] >= 0 ? reinterpret_cast<const u32x4*>(k + (int64_t)id[j] * D)[c % CPK]
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stash = [&](int b, const u32x4 (&v)[NC]) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int c = threadIdx.x + 256 * j;
+      if (c < 32 * CPK) *reinterpret_cast<u32x4*>(&tile[b][(c / CPK) * RB + (c % CPK) * 16]) = v[j];
+    }
+  };
+  int id_cur[NC], id_next[NC];
+  u32x4 v[NC];
+  fetch_ids(0, id_cur);
+  fetch_ids(32, id_next);
+  fetch_keys(id_cur, v);
+  bf16x8 a[1][MT][KS];
+  float wv[MT][16];
+  load_q_frag<MT, KS>(q, rq, H, true, a[0]);
+  load_w_frag<MT>(w, w_stride, rq, H, true, wv);
+  const float tau = top_score[(int64_t)rq * topk + topk - 1];
+  stash(0, v);
+  __syncthreads();
+  for (int it = 0; it * 32 < n; ++it) {
+    const int t0 = it * 32;
+    const bool more = t0 + 32 < n;
+    if (more) {
+      fetch_keys(id_next, v);
+      fetch_ids(t0 + 64, id_next);
+    }
+    if (active) {
+      f32x16 acc[1][MT];
+      const unsigned char* kr = &tile[it & 1][(lane & 31) * RB];
+      mfma_tiles<1, MT, KS>(
+          a,
+          [&](int s) {
+            return as_bf16x8(*reinterpret_cast<const u32x4*>(kr + (2 * s + (lane >> 5)) * 16));
+          },
+          acc);
+      const float sc = head_reduce<MT>(acc[0], wv);
+      const int i = t0 + (lane & 31);
+      const bool keep = lane < 32 && i < n && sc >= tau;
+      const int slot = wave_append(keep, &kept_cnt[r]);
+      if (keep) {
+        kept_score[(int64_t)r * cap + slot] = sc;
+        kept_id[(int64_t)r * cap + slot] = ids[i];
+      }
+    }
+    if (more) stash((it + 1) & 1, v);
+    __syncthreads();
+  }
+}
+
 // First K of (seed top-K) u (kept survivors) by (score desc, key asc).
-constexpr int kMergeThreads = 256;
+constexpr int kMergeThreads = 1024;
 __global__ __launch_bounds__(kMergeThreads) void dosa_merge(
     const DosaCtx* ctx, const int32_t* __restrict__ row_fb, const int32_t* __restrict__ top_idx,
     const float* __restrict__ top_score, int topk, const float* __restrict__ kept_score,
@@ -823,14 +1052,15 @@ __global__ __launch_bounds__(1024) void dosa_fallback_list(DosaCtx* ctx, const i
 }
 
 __global__ void dosa_stats(const DosaCtx* ctx, const float* top_score, int topk,
-                           const int32_t* bitmap_cnt_unused, const int32_t* surv_cnt,
+                           const int32_t* shared_n, const int32_t* surv_cnt,
                            const int32_t* row_fb, int n_q, float* tau, int32_t* n_surv,
-                           int32_t* fallback) {
+                           int32_t* fallback, int32_t* n_shared) {
   for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < n_q; r += gridDim.x * blockDim.x) {
     const int all = ctx->global_fallback;
     if (tau) tau[r] = all ? __builtin_nanf("") : top_score[(int64_t)r * topk + topk - 1];
     if (n_surv) n_surv[r] = all ? -1 : surv_cnt[r];
     if (fallback) fallback[r] = (all || row_fb[r]) ? 1 : 0;
+    if (n_shared) n_shared[r] = (all || !shared_n) ? 0 : shared_n[r];
   }
 }
 
@@ -914,12 +1144,26 @@ static hipError_t run_dosa(const uint16_t* q, const uint16_t* k, const float* w,
             F(L.knorm), reinterpret_cast<const uint32_t*>(ws + L.seed_mask), vis, n_q, n_k,
             reinterpret_cast<uint32_t*>(ws + L.bitmap), words, nseg, seg_keys));
   }
-  SI_TRY((dosa_compact, dim3(n_q), dim3(kCompThreads), 0, st, ctx,
-          reinterpret_cast<const uint32_t*>(ws + L.bitmap), words, vis, n_k, cap, I(L.surv_ids),
-          I(L.surv_cnt), I(L.row_fb)));
+  const bool groups = p->shared_streams != 0;
+  const int n_groups = (n_q + kGroupRows - 1) / kGroupRows;
+  if (groups) {
+    SI_TRY((dosa_compact_groups, dim3(n_groups), dim3(kCompThreads), 0, st, ctx,
+            reinterpret_cast<const uint32_t*>(ws + L.bitmap), words, vis, n_q, n_k, cap,
+            I(L.shared_ids), I(L.shared_cnt), I(L.surv_ids), I(L.solo_cnt), I(L.surv_cnt),
+            I(L.shared_n), I(L.row_fb)));
+  } else {
+    SI_TRY((dosa_compact, dim3(n_q), dim3(kCompThreads), 0, st, ctx,
+            reinterpret_cast<const uint32_t*>(ws + L.bitmap), words, vis, n_k, cap,
+            I(L.surv_ids), I(L.surv_cnt), I(L.row_fb)));
+  }
   SI_TRY(((dosa_rescore<MT, KS>), dim3(n_q), dim3(256), 0, st, ctx, q, w, wst, H, k, F(L.top_score),
-          topk, I(L.surv_ids), I(L.surv_cnt), I(L.row_fb), cap, F(L.kept_score), I(L.kept_id),
-          I(L.kept_cnt)));
+          topk, I(L.surv_ids), I(groups ? L.solo_cnt : L.surv_cnt), I(L.row_fb), cap,
+          F(L.kept_score), I(L.kept_id), I(L.kept_cnt)));
+  if (groups)
+    SI_TRY(((dosa_rescore_shared<MT, KS>), dim3(n_groups, kSharedSplit), dim3(256), 0, st, ctx,
+            q, w, wst, n_q,
+            H, k, F(L.top_score), topk, I(L.shared_ids), I(L.shared_cnt), I(L.row_fb), cap,
+            F(L.kept_score), I(L.kept_id), I(L.kept_cnt)));
   SI_TRY((dosa_merge, dim3(n_q), dim3(kMergeThreads), 0, st, ctx, I(L.row_fb), I(L.top_idx),
           F(L.top_score), topk, F(L.kept_score), I(L.kept_id), I(L.kept_cnt), cap, out_idx,
           out_score));
@@ -940,10 +1184,10 @@ static hipError_t run_dosa(const uint16_t* q, const uint16_t* k, const float* w,
     e = launch_topk(ta, st);
     if (e != hipSuccess) return e;
   }
-  if (stats && (stats->tau || stats->n_survivors || stats->fallback))
+  if (stats && (stats->tau || stats->n_survivors || stats->fallback || stats->n_shared))
     SI_TRY((dosa_stats, dim3(grid_for(n_q, 256)), dim3(256), 0, st, ctx, F(L.top_score), topk,
-            nullptr, I(L.surv_cnt), I(L.row_fb), n_q, stats->tau, stats->n_survivors,
-            stats->fallback));
+            groups ? I(L.shared_n) : nullptr, I(L.surv_cnt), I(L.row_fb), n_q, stats->tau,
+            stats->n_survivors, stats->fallback, stats->n_shared));
   return hipSuccess;
 }
 
@@ -972,7 +1216,8 @@ extern "C" si_status dosa_prune_topk(const void* q, const void* k, si_dtype dtyp
       p->n_rep_queries > kMaxRep || p->rep_topk < 1 || p->rep_topk > kMaxTopk ||
       p->kept_heads < 0 || p->kept_heads > 31 || p->kept_heads > H ||
       p->survivor_capacity < 1 || p->survivor_capacity > kMaxCapacity ||
-      !(p->neg_active_frac == p->neg_active_frac))
+      !(p->neg_active_frac == p->neg_active_frac) || p->shared_streams < 0 ||
+      p->shared_streams > 1)
     return SI_ERR_INVALID_ARGUMENT;
   if (dtype != SI_BF16) return SI_ERR_UNSUPPORTED_DTYPE;
   if (n_q == 0) return SI_OK;

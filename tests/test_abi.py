@@ -209,6 +209,7 @@ def test_dosa_refusals(L):
     assert call(DosaParams(16, 4, 8, 33, 0.5, None, 64)) == INVALID  # kept_heads > H
     assert call(DosaParams(16, 65, 8, 8, 0.5, None, 64)) == INVALID  # > 64 representatives
     assert call(DosaParams(100, 4, 8, 8, 0.5, None, 64)) == INVALID  # n_seeds > n_k
+    assert call(DosaParams(16, 4, 8, 8, 0.5, None, 64, 2)) == INVALID  # shared_streams not 0/1
     assert call(DosaParams(16, 4, 8, 8, 0.5, None, 8193)) == INVALID  # capacity > 8192
     assert call(DosaParams(16, 4, 8, 8, 0.5, None, 0)) == INVALID  # capacity
     assert call(good, dtype=0) == DTYPE
