@@ -28,9 +28,10 @@ namespace si {
 //     item's output slot is its bin's offset plus the number of same-bin
 //     items ahead of it under (score desc, index asc), counted over the bin
 //     four entries at a time (entries past the bin belong to lower bins or
-//     are zero, so they never count).  The ordered row is staged in LDS and
-//     written coalesced.  If some bin holds more than kCrowd selected items
-//     (heavy ties, very uneven scores) the row is ordered by a bitonic sort.
+//     are zero, so they never count), and the item is written straight to
+//     that slot of the output row.  If some bin holds more than kCrowd
+//     selected items (heavy ties, very uneven scores) the row is ordered by
+//     a bitonic sort in LDS and written from there.
 // Staged items are 64-bit composites: order key << 32 | bin << 13 |
 // (8191 - position); composites compare as (score desc, index asc), and the
 // bin rides along so the rank step need not recompute it.
@@ -160,11 +161,10 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   // A. load.  A NaN score is taken as -inf (its order is unspecified; this
   //    makes every comparison below a total preorder on floats, -0 == +0).
   //    Every position is loaded through a buffer resource bounded at the
-  //    row's end, so the 32 loads go out unconditionally and a position past
-  //    the end reads 0.  Those zeros take part in the value range (which
-  //    then covers 0 as well: still a valid range, at worst a coarser one)
-  //    and the registers are never rewritten; only the bin counts and the
-  //    selection mask them out.
+  //    row's end, so a position past the end reads 0.  Those zeros take
+  //    part in the value range (which then covers 0 as well: still a valid
+  //    range, at worst a coarser one) and the registers are never
+  //    rewritten; only the bin counts and the selection mask them out.
 #pragma unroll
   for (int k = 0; k < kBins / (4 * kBT); ++k)
     *reinterpret_cast<uint4*>(&sm.bins[4 * t + 4 * kBT * k]) = make_uint4(0u, 0u, 0u, 0u);
@@ -182,13 +182,34 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, n * 4, kRowBufWord3);
-    // each offset is made opaque so that no two loads are merged into a
-    // multi-dword access (whose bounds check need not be per dword)
+    // Group rows wholly inside the row (j < gfull, the same for every
+    // thread) are read as one 16-byte load per thread when the row is
+    // 16-byte aligned; the partly visible group row dword by dword, each
+    // offset made opaque so that no two are merged into a multi-dword
+    // access (whose bounds check need not be per dword); group rows past
+    // the end hold zeros, as a load past the end would.
+    const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
 #pragma unroll
-    for (int i = 0; i < kBPer; ++i) {
-      int o = 4 * pos_of(i);
-      asm volatile("" : "+v"(o));
-      x[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0));
+    for (int j = 0; j < kBGroups; ++j) {
+      if (vec && j < gfull) {
+        typedef uint32_t w4 __attribute__((ext_vector_type(4)));
+        const w4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (base + kBStep * j), 0, 0);
+        x[4 * j + 0] = __uint_as_float(v[0]);
+        x[4 * j + 1] = __uint_as_float(v[1]);
+        x[4 * j + 2] = __uint_as_float(v[2]);
+        x[4 * j + 3] = __uint_as_float(v[3]);
+      } else if (j < gused) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          int o = 4 * pos_of(4 * j + c);
+          asm volatile("" : "+v"(o));
+          x[4 * j + c] =
+              __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0));
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[4 * j + c] = 0.0f;
+      }
     }
   }
   float vlo = __builtin_inff(), vhi = -__builtin_inff();
@@ -453,55 +474,47 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   }
   __syncthreads();
 
-  // G. order: rank inside the bin.  After the scatter a bin's packed word is
-  //    ((offset + count) << 16 | count).
+  // G+H. order and output.  Each selected item's slot is its bin's offset
+  //    plus the number of same-bin items ahead of it under (score desc,
+  //    index asc); items are written straight to that slot of the output
+  //    row (a bin's items sit next to each other, so a wave's stores stay
+  //    close to consecutive), and the slots past cnt get the padding.
+  //    After the scatter a bin's packed word is ((offset + count) << 16 |
+  //    count).  Positions are < n by construction; the clamp only keeps an
+  //    id_map lookup in bounds.
+  auto emit = [&](int slot, uint64_t c) {
+    uint32_t p = kPosMask - ((uint32_t)c & kPosMask);
+    p = p < (uint32_t)n ? p : 0u;
+    oi[slot] = idmap ? idmap[p] : (int32_t)(start + p);
+    if (os) os[slot] = key_to_float((uint32_t)(c >> 32));
+  };
   if (crowd <= (uint32_t)kCrowd) {
-    uint64_t it[kBK / kBT];
-    uint32_t dst[kBK / kBT];
 #pragma unroll
     for (int m = 0; m < kBK / kBT; ++m) {
       const int q = t + kBT * m;
-      it[m] = 0ull;
-      dst[m] = 0u;
       if (q < cnt) {
-        it[m] = sm.x.comp[q];
-        const uint32_t w = sm.bins[((uint32_t)it[m] >> kPosBits) & (kBins - 1)];
+        const uint64_t it = sm.x.comp[q];
+        const uint32_t w = sm.bins[((uint32_t)it >> kPosBits) & (kBins - 1)];
         const uint32_t len = w & 0xFFFFu, s0 = (w >> 16) - len;
         const uint64_t* e = &sm.x.comp[s0];
         uint32_t rk = 0u;
-        for (uint32_t j = 0; j < len; j += 4) {
-          rk += (uint32_t)(e[j] > it[m]) + (uint32_t)(e[j + 1] > it[m]) +
-                (uint32_t)(e[j + 2] > it[m]) + (uint32_t)(e[j + 3] > it[m]);
+        for (uint32_t jj = 0; jj < len; jj += 4) {
+          rk += (uint32_t)(e[jj] > it) + (uint32_t)(e[jj + 1] > it) +
+                (uint32_t)(e[jj + 2] > it) + (uint32_t)(e[jj + 3] > it);
         }
-        dst[m] = s0 + rk;
+        emit((int)(s0 + rk), it);
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < kBK / kBT; ++m)
-      if (t + kBT * m < cnt) sm.x.comp[dst[m]] = it[m];
-    __syncthreads();
   } else {
     const int P = next_pow2(cnt);
     for (int q = cnt + t; q < P; q += kBT) sm.x.comp[q] = 0ull;
     __syncthreads();
     bitonic_sort_desc<kBT>(sm.x.comp, P);
+    for (int q = t; q < cnt; q += kBT) emit(q, sm.x.comp[q]);
   }
-
-  // H. coalesced output of the ordered row, then the padding.  Positions
-  //    are < n by construction; the clamp only keeps an id_map lookup in
-  //    bounds.
-  for (int q = t; q < K; q += kBT) {
-    if (q < cnt) {
-      const uint64_t c = sm.x.comp[q];
-      uint32_t p = kPosMask - ((uint32_t)c & kPosMask);
-      p = p < (uint32_t)n ? p : 0u;
-      oi[q] = idmap ? idmap[p] : (int32_t)(start + p);
-      if (os) os[q] = key_to_float((uint32_t)(c >> 32));
-    } else {
-      oi[q] = -1;
-      if (os) os[q] = -__builtin_inff();
-    }
+  for (int q = cnt + t; q < K; q += kBT) {
+    oi[q] = -1;
+    if (os) os[q] = -__builtin_inff();
   }
 }
 
