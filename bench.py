@@ -167,6 +167,14 @@ def bench_indexer(args, cfg, workload):
     wall_ms, per = timed_steps([("score_topk", score_topk), ("witness", witness)], args.steps,
                                args.warmup)
     _, st = timed_steps([("score", score), ("topk", topk)], args.steps, args.warmup)
+    # the witness kernel alone, eight launches back to back per timed step:
+    # its average launch time without the gap a single short launch carries
+    # (every launch reads the whole rows; with a budget of S every segment
+    # the first one finds empty gets its witness, so the repeats write
+    # nothing)
+    WIT_REP = 8
+    _, wt = timed_steps([("witness", lambda: [witness() for _ in range(WIT_REP)])], args.steps,
+                        args.warmup)
 
     flops = pairs * 2.0 * H * D
     kbytes = cfg["k"].nbytes + (cfg["k_scale"].nbytes if cfg["k_scale"] is not None else 0)
@@ -179,6 +187,9 @@ def bench_indexer(args, cfg, workload):
                            algo_flops=flops),
         "witness": dict(ms=per["witness"], gbs=wit_bytes / per["witness"] / 1e6,
                         algo_bytes=wit_bytes),
+        "witness_stage": dict(ms=wt["witness"] / WIT_REP,
+                              gbs=wit_bytes / (wt["witness"] / WIT_REP) / 1e6,
+                              algo_bytes=wit_bytes, launches_per_event=WIT_REP),
         "score_stage": dict(ms=st["score"], tflops=flops / st["score"] / 1e9,
                             gbs=score_bytes / st["score"] / 1e6, algo_flops=flops,
                             algo_bytes=score_bytes),
