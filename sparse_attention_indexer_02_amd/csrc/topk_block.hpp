@@ -56,7 +56,8 @@ struct alignas(16) BlockSmem {
                               // then one scratch word per lane
   union {
     uint64_t comp[kBK + 4];  // selected composites grouped by bin (+ 4 zero
-                             // entries past the last), then the ordered row
+                             // entries past the last); sorted in place when
+                             // a bin is too crowded to rank
     uint32_t sub[2048];      // refine histogram
     uint32_t list[kBrute];   // b1's values
     struct {
