@@ -219,6 +219,8 @@ struct TopkArgs {
   int64_t id_map_stride = 0;           // row r maps through id_map + r * id_map_stride
   int32_t chunk = 0;                   // > 0: block y takes positions [y chunk, (y+1) chunk)
   int64_t out_stride = 0;              // output row stride (0: K); chunk y writes at y K
+  int32_t len_levels = 0;              // row length = the visible length after this many chunk
+                                       // passes (each keeps min(K, chunk) per 8192-chunk)
   void* workspace = nullptr;           // candidate lists for rows longer than one block
   size_t workspace_bytes = 0;
 };

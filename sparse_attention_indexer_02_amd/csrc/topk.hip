@@ -5,11 +5,11 @@
 // Kernels:
 //  * topk_block: rows of at most 8192 scores, K <= 2048, one 512-thread
 //    workgroup per row holding the row in registers (steps in
-//    topk_block.hpp).  Longer
-//    rows (K <= 2048, with a workspace) are cut into 8192-score chunks whose
-//    ordered top-K lists, with the chunks' position maps, are selected from
-//    again by the same kernel until one chunk remains (topk_next_len gives
-//    each level's row lengths).
+//    topk_block.hpp).  Longer rows (K <= 2048, with a workspace) are cut
+//    into 8192-score chunks whose ordered top-K lists, with the chunks'
+//    position maps, are selected from again by the same kernel until one
+//    chunk remains (each level's row lengths follow from the original ones,
+//    TopkArgs::len_levels).
 //  * topk_rows: K > 2048, or a long row without a workspace.  One
 //    512-thread workgroup per row; rows up to 8192 scores are staged in LDS,
 //    longer ones re-read per pass; a 3-pass radix select (11/11/10-bit
@@ -106,33 +106,12 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(8))) void t
   topk_row_block(a, r, (int)blockIdx.y, S);
 }
 
-// Candidate count of each row after a chunk pass: every full chunk keeps K,
-// the last one min(K, its length).  Rows follow the same row list.
-__global__ void topk_next_len(TopkArgs a, int32_t* out_len) {
-  int r = (int)(blockIdx.x * blockDim.x + threadIdx.x);
-  if (r >= a.n_rows) return;
-  if (a.row_list) {
-    if (r >= *a.row_count) return;
-    r = a.row_list[r];
-  }
-  int64_t off;
-  const int64_t n =
-      a.vis_len ? visible_len(a.vis_len, a.k_row_offset, r, a.n_k, a.max_vis, &off) : a.max_vis;
-  int64_t c = 0;
-  if (n > 0) {
-    const int64_t full = (n - 1) / kBN;  // chunks before the last one
-    const int64_t last = n - full * kBN;
-    c = full * a.K + (last < a.K ? last : a.K);
-  }
-  out_len[r] = (int32_t)c;
-}
-
 // Bytes of one chunk level (candidate ids + scores + per-row counts), and
 // the number of chunks per row of a level with rows of at most len scores.
 static int64_t chunks_of(int64_t len) { return (len + kBN - 1) / kBN; }
 static size_t level_bytes(int64_t n_rows, int64_t len, int K) {
   const size_t cand = (size_t)n_rows * (size_t)chunks_of(len) * (size_t)K;
-  return ((cand * 8 + (size_t)n_rows * 4) + 255) & ~(size_t)255;
+  return (cand * 8 + 255) & ~(size_t)255;
 }
 
 size_t topk_workspace_bytes(int64_t n_rows, int64_t max_vis, int K) {
@@ -165,21 +144,17 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     const int64_t cstride = nch * a.K;
     int32_t* cidx = reinterpret_cast<int32_t*>(ws);
     float* csc = reinterpret_cast<float*>(ws + (size_t)a.n_rows * cstride * 4);
-    int32_t* clen = reinterpret_cast<int32_t*>(ws + (size_t)a.n_rows * cstride * 8);
     TopkArgs L = cur;
     L.chunk = kBN;
     L.out_idx = cidx;
     L.out_score = csc;
     L.out_stride = cstride;
     hipLaunchKernelGGL(topk_block, dim3((unsigned)a.n_rows, (unsigned)nch), dim3(kBT), 0, st, L);
-    hipLaunchKernelGGL(topk_next_len, dim3((unsigned)((a.n_rows + 255) / 256)), dim3(256), 0, st,
-                       cur, clen);
+    // the next level's rows: the candidates this pass keeps, at the same
+    // positions as the level's rows (lengths follow from the original ones)
     cur.scores = csc;
     cur.stride = cstride;
-    cur.vis_len = clen;
-    cur.k_row_offset = nullptr;
-    cur.n_k = cstride;
-    cur.max_vis = cstride;
+    cur.len_levels += 1;
     cur.id_map = cidx;
     cur.id_map_stride = cstride;
     ws += level_bytes(a.n_rows, len, a.K);

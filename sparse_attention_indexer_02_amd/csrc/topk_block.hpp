@@ -120,6 +120,12 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   int64_t off;
   int64_t n64 =
       a.vis_len ? visible_len(a.vis_len, a.k_row_offset, r, a.n_k, a.max_vis, &off) : a.max_vis;
+  // a chunk pass keeps min(K, chunk length) candidates of each 8192-chunk
+  for (int l = 0; l < a.len_levels; ++l) {
+    const int64_t full = n64 > 0 ? (n64 - 1) / kBN : 0;  // chunks before the last one
+    const int64_t last = n64 - full * kBN;
+    n64 = n64 > 0 ? full * a.K + (last < a.K ? last : a.K) : 0;
+  }
   const int K = a.K;
   // chunk mode: this block takes positions [start, start + chunk) of the row
   // and writes its ordered top-K at y K of the output row; an empty chunk
