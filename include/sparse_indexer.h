@@ -362,7 +362,7 @@ si_status positions_of_blocks(const int32_t* blocks, int32_t n_q, int32_t n_kv_h
  *  page_table [rows, pages_per_row] i32 physical page ids.
  *  out_slots  [rows, width] i64.
  * Errors: INVALID_ARGUMENT (negative counts, both or neither mapping,
- * page_size or pages_per_row < 1 with a page table, width > 2^26, null
+ * page_size or pages_per_row < 1 with a page table, width > 2^25, null
  * pointers).
  * ------------------------------------------------------------------------ */
 si_status gather_slots(const int32_t* idx, int32_t rows, int32_t width, const int32_t* lens,

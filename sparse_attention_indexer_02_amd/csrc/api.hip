@@ -259,7 +259,7 @@ si_status gather_slots(const int32_t* idx, int32_t rows, int32_t width, const in
                        const int64_t* row_start, const int32_t* page_table,
                        int32_t pages_per_row, int32_t page_size, int64_t* out_slots,
                        hipStream_t stream) {
-  if (rows < 0 || width < 0 || width > (1 << 26)) return SI_ERR_INVALID_ARGUMENT;
+  if (rows < 0 || width < 0 || width > (1 << 25)) return SI_ERR_INVALID_ARGUMENT;  // grid y <= 32768
   if ((row_start == nullptr) == (page_table == nullptr)) return SI_ERR_INVALID_ARGUMENT;
   if (page_table && (page_size < 1 || pages_per_row < 1)) return SI_ERR_INVALID_ARGUMENT;
   if (rows == 0 || width == 0) return SI_OK;

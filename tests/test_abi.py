@@ -250,7 +250,7 @@ def test_positions_and_gather_refusals(L):
         return L.gather_slots(i, rows, width, _p(lens), rs, pt, ppr, page, _p(slots), None)
 
     assert gcall(rows=-1) == INVALID
-    assert gcall(width=(1 << 26) + 1) == INVALID
+    assert gcall(width=(1 << 25) + 1) == INVALID
     assert gcall(rs=None) == INVALID  # neither mapping
     assert gcall(pt=_p(table)) == INVALID  # both mappings
     assert gcall(rs=None, pt=_p(table), page=0) == INVALID
