@@ -991,8 +991,10 @@ __global__ __launch_bounds__(kMergeThreads) void dosa_merge(
     const float* __restrict__ top_score, int topk, const float* __restrict__ kept_score,
     const int32_t* __restrict__ kept_id, const int32_t* __restrict__ kept_cnt, int cap,
     int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
-  __shared__ uint64_t B[kMaxCapacity];
-  __shared__ uint64_t A[kMaxTopk];
+  // dynamic LDS: B [next_pow2(cap)] kept composites, then A [topk]
+  extern __shared__ uint64_t merge_lds[];
+  uint64_t* B = merge_lds;
+  uint64_t* A = merge_lds + next_pow2(cap);
   const int r = blockIdx.x;
   if (ctx->global_fallback || row_fb[r]) return;
   const int m = kept_cnt[r];
@@ -1164,7 +1166,16 @@ static hipError_t run_dosa(const uint16_t* q, const uint16_t* k, const float* w,
             q, w, wst, n_q,
             H, k, F(L.top_score), topk, I(L.shared_ids), I(L.shared_cnt), I(L.row_fb), cap,
             F(L.kept_score), I(L.kept_id), I(L.kept_cnt)));
-  SI_TRY((dosa_merge, dim3(n_q), dim3(kMergeThreads), 0, st, ctx, I(L.row_fb), I(L.top_idx),
+  {
+    // LDS sized by the capacity and K rather than their maxima: more rows
+    // per CU
+    const size_t lds = (size_t)(next_pow2(cap) + topk) * sizeof(uint64_t);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dosa_merge),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  SI_TRY((dosa_merge, dim3(n_q), dim3(kMergeThreads),
+          (size_t)(next_pow2(cap) + topk) * sizeof(uint64_t), st, ctx, I(L.row_fb), I(L.top_idx),
           F(L.top_score), topk, F(L.kept_score), I(L.kept_id), I(L.kept_cnt), cap, out_idx,
           out_score));
   SI_TRY((dosa_fallback_list, dim3(1), dim3(1024), 0, st, ctx, I(L.row_fb), n_q, I(L.fb_list)));
