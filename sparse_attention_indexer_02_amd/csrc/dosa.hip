@@ -743,7 +743,7 @@ __device__ __forceinline__ int wave_append(bool keep, int32_t* cnt) {
 }
 
 // Exact rescoring of survivors with the shared micro-kernel (keys gathered
-// straight into the k-step layout).  One workgroup per row.
+// straight into the k-step layout, one tile ahead).  One workgroup per row.
 template <int MT, int KS>
 __global__ __launch_bounds__(256) void dosa_rescore(
     const DosaCtx* ctx, const uint16_t* __restrict__ q, const float* __restrict__ w,
@@ -762,25 +762,33 @@ __global__ __launch_bounds__(256) void dosa_rescore(
   float wv[MT][16];
   load_q_frag<MT, KS>(q, r, H, true, a[0]);
   load_w_frag<MT>(w, w_stride, r, H, true, wv);
-  for (int t0 = wave * 32; t0 < n; t0 += 4 * 32) {
+  // tiles wave * 32 + 128 i; the next tile's ids are read and its keys
+  // gathered into registers during this tile's MFMAs
+  auto gather = [&](int t0, int& id, u32x4 (&kb)[KS]) {
     const int i = t0 + (lane & 31);
-    const bool in = i < n;
-    const int id = in ? surv_ids[(int64_t)r * cap + i] : 0;
-    const u32x4* kb = reinterpret_cast<const u32x4*>(k + (int64_t)id * D);
+    id = i < n ? surv_ids[(int64_t)r * cap + i] : -1;
+    const u32x4* src = reinterpret_cast<const u32x4*>(k + (int64_t)(id >= 0 ? id : 0) * D);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      kb[s] = id >= 0 ? src[2 * s + (lane >> 5)] : u32x4{0u, 0u, 0u, 0u};
+  };
+  int id_c = -1, id_n = -1;
+  u32x4 kc[KS], kn[KS];
+  if (wave * 32 < n) gather(wave * 32, id_c, kc);
+  for (int t0 = wave * 32; t0 < n; t0 += 4 * 32) {
+    if (t0 + 128 < n) gather(t0 + 128, id_n, kn);
     f32x16 acc[1][MT];
-    mfma_tiles<1, MT, KS>(
-        a,
-        [&](int s) {
-          return as_bf16x8(in ? kb[2 * s + (lane >> 5)] : u32x4{0u, 0u, 0u, 0u});
-        },
-        acc);
+    mfma_tiles<1, MT, KS>(a, [&](int s) { return as_bf16x8(kc[s]); }, acc);
     float s = head_reduce<MT>(acc[0], wv);
-    const bool keep = lane < 32 && in && s >= tau;
+    const bool keep = lane < 32 && id_c >= 0 && s >= tau;
     const int slot = wave_append(keep, &kept_cnt[r]);
     if (keep) {
       kept_score[(int64_t)r * cap + slot] = s;
-      kept_id[(int64_t)r * cap + slot] = id;
+      kept_id[(int64_t)r * cap + slot] = id_c;
     }
+    id_c = id_n;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) kc[j] = kn[j];
   }
 }
 
