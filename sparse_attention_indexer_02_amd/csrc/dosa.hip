@@ -669,21 +669,31 @@ __global__ __launch_bounds__(256, 2) void dosa_bound(
     fetch(tn);
     side(tn, kn_n, sw_n);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the MFMAs
-    const unsigned char* brow = &lds[buf][(lane & 31) * ROWB + (lane >> 5) * 16];
-    f32x16 acc[QPW][1];
-    mfma_tiles<QPW, 1, KS>(
-        a, [&](int s) { return as_bf16x8(*reinterpret_cast<const u32x4*>(brow + 32 * s)); },
-        acc);
     const int64_t j = (int64_t)t * 32 + (lane & 31);
-    const bool seed = (sw >> (j & 31)) & 1u;
+    if (sw == 0xFFFFFFFFu) {
+      // every key of the tile is a seed (the cold prior's low-index keys
+      // mostly are): nothing survives, no bound to compute
 #pragma unroll
-    for (int i = 0; i < QPW; ++i) {
-      float u = head_reduce<1>(acc[i], wv[i]) + cr[i] * kn;
-      bool pass = lane < 32 && j < vis[i] && !seed && u >= tau[i];
-      uint64_t m = __ballot(pass);
-      int r = r0 + wave * QPW + i;
-      if (lane == 0 && r < n_q && (int64_t)t * 32 < vis[i])
-        bitmap[(int64_t)r * words + t] = (uint32_t)m;
+      for (int i = 0; i < QPW; ++i) {
+        const int r = r0 + wave * QPW + i;
+        if (lane == 0 && r < n_q && (int64_t)t * 32 < vis[i]) bitmap[(int64_t)r * words + t] = 0u;
+      }
+    } else {
+      const unsigned char* brow = &lds[buf][(lane & 31) * ROWB + (lane >> 5) * 16];
+      f32x16 acc[QPW][1];
+      mfma_tiles<QPW, 1, KS>(
+          a, [&](int s) { return as_bf16x8(*reinterpret_cast<const u32x4*>(brow + 32 * s)); },
+          acc);
+      const bool seed = (sw >> (j & 31)) & 1u;
+#pragma unroll
+      for (int i = 0; i < QPW; ++i) {
+        float u = head_reduce<1>(acc[i], wv[i]) + cr[i] * kn;
+        bool pass = lane < 32 && j < vis[i] && !seed && u >= tau[i];
+        uint64_t m = __ballot(pass);
+        int r = r0 + wave * QPW + i;
+        if (lane == 0 && r < n_q && (int64_t)t * 32 < vis[i])
+          bitmap[(int64_t)r * words + t] = (uint32_t)m;
+      }
     }
     // buffer buf ^ 1 held tile t - 1, read before the previous barrier
     stash(buf ^ 1);
