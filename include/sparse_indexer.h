@@ -4,6 +4,7 @@
  *
  * Operations, each defined by the page cited at its declaration:
  *   idx_score_topk       lightning-indexer score + per-query top-K
+ *   idx_score_topk_witness idx_score_topk then kvwitness_merge, in one pass
  *   idx_score_topk_prior the same result on the decode path, selecting only
  *                        among keys above a threshold from recent keys
  *   dosa_prune_topk      the same top-K through DoSA's certified prune
@@ -108,6 +109,29 @@ si_status idx_score_topk(const void* q, si_dtype q_dtype, const void* k, si_dtyp
                          int32_t* out_idx, float* out_score, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 size_t idx_score_topk_workspace(int32_t n_q, int32_t H, int32_t D, int64_t max_vis, int32_t topk);
+
+/* ------------------------------------------------------------------------ *
+ * idx_score_topk_witness
+ *
+ * idx_score_topk followed by kvwitness_merge on its output rows (the
+ * "Segment Witnesses" page, Implementation rule and contracts, applied to
+ * the learned top-K rows), with the merge done by the top-K kernel on each
+ * row as it is written: out_idx equals idx_score_topk's out_idx after
+ * kvwitness_merge(out_idx, n_q, topk, context_lens, num_segments, keep,
+ * max_replacements), bit for bit; out_score is idx_score_topk's (the merge
+ * changes ids only).  Arguments as the two calls; the merge's refusals are
+ * checked first, in its order, then the indexer's.  num_segments == 0 or a
+ * budget of 0 gives idx_score_topk's result.  The workspace is
+ * idx_score_topk_workspace's.
+ * ------------------------------------------------------------------------ */
+si_status idx_score_topk_witness(const void* q, si_dtype q_dtype, const void* k, si_dtype k_dtype,
+                                 const float* k_scale, const float* w, int64_t w_row_stride,
+                                 const int64_t* k_row_offset, const int32_t* vis_len, int32_t n_q,
+                                 int32_t H, int32_t D, int64_t n_k, int64_t max_vis, int32_t topk,
+                                 int32_t* out_idx, float* out_score,
+                                 const int32_t* context_lens, int32_t num_segments, int32_t keep,
+                                 int32_t max_replacements, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * idx_score_topk_prior

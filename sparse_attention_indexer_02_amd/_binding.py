@@ -46,6 +46,8 @@ SIGNATURES = {
     "idx_score_topk": (i32, [vp, i32, vp, i32, vp, vp, i64, vp, vp, i32, i32, i32, i64, i64, i32,
                              vp, vp, vp, sz, vp]),
     "idx_score_topk_workspace": (sz, [i32, i32, i32, i64, i32]),
+    "idx_score_topk_witness": (i32, [vp, i32, vp, i32, vp, vp, i64, vp, vp, i32, i32, i32, i64,
+                                     i64, i32, vp, vp, vp, i32, i32, i32, vp, sz, vp]),
     "idx_score_topk_prior": (i32, [vp, i32, vp, i32, vp, vp, i64, vp, vp, i32, i32, i32, i64, i64,
                                    i32, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
     "idx_score_topk_prior_workspace": (sz, [i32, i64, i32]),
@@ -161,6 +163,43 @@ def idx_score_topk(q, k, w, vis_len, topk, *, k_scale=None, k_row_offset=None, m
                               _ptr(vis_len), n_q, H, D, n_k, max_vis, topk, _ptr(out_idx),
                               _ptr(out_score), _ptr(ws), ws_bytes, _stream(dev))
     _check(st, "idx_score_topk")
+    return out_idx, out_score
+
+
+def idx_score_topk_witness(q, k, w, vis_len, topk, context_lens, num_segments, *, keep=None,
+                           max_replacements=None, k_scale=None, k_row_offset=None, max_vis=None,
+                           out_idx=None, out_score=None, want_scores=True, workspace=None):
+    """idx_score_topk then the segment-witness merge of its rows, in one pass;
+    keep/max_replacements default to the serving convention (topk - S, S).
+    Returns (idx, scores|None)."""
+    _dev_tensor(q, "q")
+    _dev_tensor(k, "k")
+    _dev_tensor(w, "w", torch.float32)
+    _dev_tensor(vis_len, "vis_len", torch.int32)
+    _dev_tensor(context_lens, "context_lens", torch.int32)
+    dev = q.device
+    n_q, H, D = q.shape
+    n_k = k.shape[0]
+    if keep is None:
+        keep = max(topk - num_segments, 0)
+    if max_replacements is None:
+        max_replacements = num_segments
+    if max_vis is None:
+        max_vis = n_k if k_row_offset is None else (int(vis_len.max().item()) if n_q else 0)
+    w_stride = H if w.dim() == 2 else 0
+    if out_idx is None:
+        out_idx = torch.empty((n_q, topk), dtype=torch.int32, device=dev)
+    if out_score is None and want_scores:
+        out_score = torch.empty((n_q, topk), dtype=torch.float32, device=dev)
+    need = lib().idx_score_topk_workspace(n_q, H, D, max_vis, topk)
+    ws, ws_bytes = _workspace(need, dev, workspace)
+    st = lib().idx_score_topk_witness(_ptr(q), _dtype_code(q, "q"), _ptr(k), _dtype_code(k, "k"),
+                                      _ptr(k_scale), _ptr(w), w_stride, _ptr(k_row_offset),
+                                      _ptr(vis_len), n_q, H, D, n_k, max_vis, topk,
+                                      _ptr(out_idx), _ptr(out_score), _ptr(context_lens),
+                                      num_segments, keep, max_replacements, _ptr(ws), ws_bytes,
+                                      _stream(dev))
+    _check(st, "idx_score_topk_witness")
     return out_idx, out_score
 
 

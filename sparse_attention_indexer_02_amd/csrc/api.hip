@@ -151,6 +151,54 @@ si_status idx_score_topk(const void* q, si_dtype q_dtype, const void* k, si_dtyp
   return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
 }
 
+si_status idx_score_topk_witness(const void* q, si_dtype q_dtype, const void* k, si_dtype k_dtype,
+                                 const float* k_scale, const float* w, int64_t w_row_stride,
+                                 const int64_t* k_row_offset, const int32_t* vis_len, int32_t n_q,
+                                 int32_t H, int32_t D, int64_t n_k, int64_t max_vis, int32_t topk,
+                                 int32_t* out_idx, float* out_score,
+                                 const int32_t* context_lens, int32_t num_segments, int32_t keep,
+                                 int32_t max_replacements, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  // the merge's refusals first, in kvwitness_merge's order, then the
+  // indexer's; a refused call writes nothing
+  if (n_q < 0 || topk < 0 || keep < 0 || max_replacements < 0) return SI_ERR_INVALID_ARGUMENT;
+  if (n_q > 0 && !context_lens) return SI_ERR_ROWS_MISMATCH;
+  if (n_q > 0 && topk > 0 && !out_idx) return SI_ERR_INVALID_ARGUMENT;
+  if (num_segments < 0 || num_segments > SI_MAX_TOPOLOGY_SEGMENTS)
+    return SI_ERR_SEGMENTS_OUT_OF_RANGE;
+  if (keep > topk) return SI_ERR_LEARNED_KEEP_OUT_OF_RANGE;
+  const int32_t B = max_replacements < topk - keep ? max_replacements : topk - keep;
+  if (num_segments == 0 || B == 0)
+    return idx_score_topk(q, q_dtype, k, k_dtype, k_scale, w, w_row_stride, k_row_offset,
+                          vis_len, n_q, H, D, n_k, max_vis, topk, out_idx, out_score, workspace,
+                          workspace_bytes, stream);
+  if (n_q > 0 && !aligned4(context_lens)) return SI_ERR_INVALID_ARGUMENT;
+  ScoreArgs sa;
+  si_status s = check_score_args(q, q_dtype, k, k_dtype, k_scale, w, w_row_stride, k_row_offset,
+                                 vis_len, n_q, H, D, n_k, max_vis, &sa);
+  if (s != SI_OK) return s;
+  if (topk < 1 || topk > kMaxTopk) return SI_ERR_INVALID_ARGUMENT;
+  if (n_q == 0) return SI_OK;
+  if (!out_idx || !aligned4(out_idx) || (out_score && !aligned4(out_score)))
+    return SI_ERR_INVALID_ARGUMENT;
+  const size_t need = idx_score_topk_workspace(n_q, H, D, max_vis, topk);
+  if (need && (!workspace || workspace_bytes < need ||
+               (reinterpret_cast<uintptr_t>(workspace) & 255)))
+    return SI_ERR_WORKSPACE_TOO_SMALL;
+  sa.scores = reinterpret_cast<float*>(workspace);
+  const size_t cand_off = (score_ws_bytes(n_q, max_vis) + 255) & ~(size_t)255;
+  TopkArgs ta;
+  ta.scores = sa.scores; ta.stride = max_vis; ta.vis_len = vis_len; ta.k_row_offset = k_row_offset;
+  ta.n_k = n_k; ta.max_vis = max_vis; ta.n_rows = n_q; ta.K = topk; ta.out_idx = out_idx;
+  ta.out_score = out_score; ta.id_map = nullptr;
+  ta.workspace = static_cast<unsigned char*>(workspace) + cand_off;
+  ta.workspace_bytes = workspace_bytes - cand_off;
+  ta.wit_lens = context_lens; ta.wit_S = num_segments; ta.wit_keep = keep; ta.wit_B = B;
+  hipError_t e = launch_score(sa, stream);
+  if (e == hipSuccess) e = launch_topk(ta, stream);
+  return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
+}
+
 size_t idx_score_topk_prior_workspace(int32_t n_q, int64_t max_vis, int32_t topk) {
   if (n_q <= 0 || max_vis <= 0 || max_vis > INT32_MAX || topk < 1 || topk > kMaxTopk) return 0;
   return prior_workspace_bytes(n_q, max_vis, topk);

@@ -221,6 +221,10 @@ struct TopkArgs {
   int64_t out_stride = 0;              // output row stride (0: K); chunk y writes at y K
   int32_t len_levels = 0;              // row length = the visible length after this many chunk
                                        // passes (each keeps min(K, chunk) per 8192-chunk)
+  // optional segment-witness merge of each final output row (context
+  // lengths, S, keep, budget B = min(max_replacements, K - keep))
+  const int32_t* wit_lens = nullptr;
+  int32_t wit_S = 0, wit_keep = 0, wit_B = 0;
   void* workspace = nullptr;           // candidate lists for rows longer than one block
   size_t workspace_bytes = 0;
 };

@@ -131,7 +131,12 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   const size_t need = topk_workspace_bytes(a.n_rows, a.max_vis, a.K);
   if (a.K > kBK || a.workspace == nullptr || a.workspace_bytes < need) {
     hipLaunchKernelGGL(topk_rows, grid, dim3(kTopkThreads), 0, st, a);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    // this kernel has no fused witness merge: the merge kernel follows
+    // (row lists do not occur with a witness merge)
+    if (e == hipSuccess && a.wit_lens)
+      e = launch_witness(a.out_idx, a.n_rows, a.K, a.wit_lens, a.wit_S, a.wit_keep, a.wit_B, st);
+    return e;
   }
   // chunk passes until a row's candidates fit one block, then the last pass
   TopkArgs cur = a;

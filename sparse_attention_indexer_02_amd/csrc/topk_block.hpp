@@ -3,7 +3,7 @@
 // top-K stage and its chunk passes).
 #pragma once
 
-#include "si_internal.hpp"
+#include "witness_seg.hpp"
 
 namespace si {
 
@@ -105,6 +105,7 @@ struct TopkSmem {
   int red[kBT / 64 + 8];
   float fred[2][kBT / 64];
   uint32_t crowd;  // largest selected count of a bin
+  uint32_t occ[2];  // fused witness merge: the row's segment occupancy
   int lcount;
 };
 
@@ -144,10 +145,21 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   int32_t* oi = a.out_idx + obase;
   float* os = a.out_score ? a.out_score + obase : nullptr;
   const int32_t* idmap = a.id_map ? a.id_map + (int64_t)r * a.id_map_stride + start : nullptr;
+  // fused witness merge of a final row: the segment bits of the ids
+  // written, OR-reduced once the row is out
+  const bool wit = a.wit_lens != nullptr && a.chunk == 0;
+  const int32_t wL = wit ? a.wit_lens[r] : 0;
+  const uint32_t wS = (uint32_t)a.wit_S;
+  const uint32_t wSe = wL > 0 ? (wS < (uint32_t)wL ? wS : (uint32_t)wL) : 0u;
+  const float wrcp = wL > 0 ? 1.0f / (float)wL : 0.0f;
   if (n <= 0) {
     for (int q = t; q < K; q += kBT) {
       oi[q] = -1;
       if (os) os[q] = -__builtin_inff();
+    }
+    if (wit && wL > 0) {  // an empty row: every segment takes its witness
+      __syncthreads();
+      if (wid == 0) write_witnesses(oi, 0ull, (uint32_t)wL, wSe, a.wit_keep, a.wit_B);
     }
     return;
   }
@@ -178,6 +190,8 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   if (t == 0) {
     lcount = 0;
     S.crowd = 0u;
+    S.occ[0] = 0u;
+    S.occ[1] = 0u;
   }
   // (adding +0 also turns -0 into +0, so the keys below need no fold)
   auto clean = [](float v) { return v == v ? v + 0.0f : -__builtin_inff(); };
@@ -489,11 +503,14 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   //    After the scatter a bin's packed word is ((offset + count) << 16 |
   //    count).  Positions are < n by construction; the clamp only keeps an
   //    id_map lookup in bounds.
+  uint64_t occ = 0ull;
   auto emit = [&](int slot, uint64_t c) {
     uint32_t p = kPosMask - ((uint32_t)c & kPosMask);
     p = p < (uint32_t)n ? p : 0u;
-    oi[slot] = idmap ? idmap[p] : (int32_t)(start + p);
+    const int32_t id = idmap ? idmap[p] : (int32_t)(start + p);
+    oi[slot] = id;
     if (os) os[slot] = key_to_float((uint32_t)(c >> 32));
+    if (wL > 0) occ |= seg_bit(id, (uint32_t)wL, wS, wSe, wrcp);
   };
   if (crowd <= (uint32_t)kCrowd) {
 #pragma unroll
@@ -522,6 +539,20 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   for (int q = cnt + t; q < K; q += kBT) {
     oi[q] = -1;
     if (os) os[q] = -__builtin_inff();
+  }
+  if (wit && wL > 0) {  // the same for every thread of the row
+    const uint32_t lo = __ockl_wfred_or_u32((uint32_t)occ);
+    const uint32_t hi = __ockl_wfred_or_u32((uint32_t)(occ >> 32));
+    if (lane == 0) {
+      if (lo) atomicOr(&S.occ[0], lo);
+      if (hi) atomicOr(&S.occ[1], hi);
+    }
+    // (the barrier also orders this row's output writes before the
+    // witnesses that overwrite some of them)
+    __syncthreads();
+    if (wid == 0)
+      write_witnesses(oi, ((uint64_t)S.occ[1] << 32) | S.occ[0], (uint32_t)wL, wSe, a.wit_keep,
+                      a.wit_B);
   }
 }
 

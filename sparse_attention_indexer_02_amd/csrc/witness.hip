@@ -2,60 +2,16 @@
 // Implementation rule and contracts).
 //
 // One wave per row.  Lanes stream the row with 16-byte loads and OR each
-// entry's segment bit into a 64-bit occupancy mask; the mask is OR-reduced
-// across the wave; lane s (< S_eff) then owns segment s: if it is empty its
-// witness e_s = ceil(s L / S_eff) takes slot keep + (number of empty segments
-// below s), when that rank is < B.  Only those <= B slots are written.
-//
-// The segment of an in-range entry, floor(x S_eff / L), comes from an fp32
-// quotient estimate corrected once each way with exact integer arithmetic
-// (the estimate is within 1 of the true floor: the quotient is below 64 and
-// the relative error of the estimate is a few 2^-24); rows with L < 2^26
-// do it in 32 bits, longer ones in 64.
-#include "si_internal.hpp"
+// entry's segment bit (witness_seg.hpp) into a 64-bit occupancy mask; the
+// mask is OR-reduced across the wave; lane s (< S_eff) then owns segment s:
+// if it is empty its witness e_s = ceil(s L / S_eff) takes slot keep +
+// (number of empty segments below s), when that rank is < B.  Only those
+// <= B slots are written.
+#include "witness_seg.hpp"
 
 namespace si {
 
 constexpr int kWitThreads = 256;
-
-__device__ __forceinline__ uint64_t seg_bit(int32_t x, uint32_t L, uint32_t S, uint32_t Se,
-                                            float rcpL) {
-  if (x < 0) return 0ull;  // padding marks no segment
-  uint32_t ux = (uint32_t)x;
-  uint32_t seg;
-  if (ux >= L) {
-    // min(floor(x S_eff / L), S - 1): S - 1 when S_eff == S, else x itself
-    // (S_eff == L), clamped.
-    seg = (Se == S) ? S - 1 : (ux < S - 1 ? ux : S - 1);
-  } else {
-    uint64_t num = (uint64_t)ux * Se;
-    uint32_t est = (uint32_t)((float)num * rcpL);
-    int64_t rem = (int64_t)num - (int64_t)est * (int64_t)L;
-    if (rem < 0) --est;
-    else if (rem >= (int64_t)L) ++est;
-    seg = est;
-  }
-  return 1ull << seg;
-}
-
-// The same segment for rows with L < 2^26, where x * S_eff < 2^32: the
-// product, the estimate's back-multiplication and the remainder all fit 32
-// bits (est * L <= num + L < 2^32), so the correction needs no 64-bit math.
-__device__ __forceinline__ uint64_t seg_bit32(int32_t x, uint32_t L, uint32_t S, uint32_t Se,
-                                              float rcpL) {
-  const uint32_t ux = (uint32_t)x;
-  uint32_t seg;
-  if (ux >= L) {
-    seg = (Se == S) ? S - 1 : (ux < S - 1 ? ux : S - 1);
-  } else {
-    const uint32_t num = ux * Se;
-    uint32_t est = (uint32_t)((float)num * rcpL);
-    const int32_t rem = (int32_t)(num - est * L);
-    est = rem < 0 ? est - 1 : (rem >= (int32_t)L ? est + 1 : est);
-    seg = est;
-  }
-  return x < 0 ? 0ull : 1ull << seg;
-}
 
 __global__ __launch_bounds__(kWitThreads) void witness_merge(int32_t* __restrict__ idx, int rows,
                                                              int topk,
@@ -107,16 +63,7 @@ __global__ __launch_bounds__(kWitThreads) void witness_merge(int32_t* __restrict
   for (int t = t0 + lane; t < topk; t += 64) occ |= seg_bit(row[t], L, S, Se, rcpL);
   occ = ((uint64_t)__ockl_wfred_or_u32((uint32_t)(occ >> 32)) << 32) |
         __ockl_wfred_or_u32((uint32_t)occ);
-
-  const bool empty = (uint32_t)lane < Se && !((occ >> lane) & 1ull);
-  const uint64_t emask = __ballot(empty);
-  if (empty) {
-    const int rank = __popcll(emask & ((1ull << lane) - 1ull));
-    if (rank < B) {
-      const uint64_t e = ((uint64_t)lane * L + Se - 1) / Se;  // ceil(s L / S_eff)
-      row[keep + rank] = (int32_t)e;
-    }
-  }
+  write_witnesses(row, occ, L, Se, keep, B);
 }
 
 hipError_t launch_witness(int32_t* idx, int32_t rows, int32_t topk, const int32_t* lens,

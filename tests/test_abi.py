@@ -118,6 +118,54 @@ def test_idx_score_topk_refusals(L):
     np.testing.assert_array_equal(outs, 7.0)
 
 
+def test_idx_score_topk_witness_refusals(L):
+    """The merge's refusals first, in kvwitness_merge's order, then the
+    indexer's; the off switch and a zero budget fall back to idx_score_topk's
+    checks; a refused call writes nothing."""
+    n_q, H, D, n_k, K = 4, 64, 128, 100, 16
+    q = np.zeros(n_q * H * D + 8, np.uint16)
+    k = np.zeros(n_k * D + 8, np.uint16)
+    w = np.zeros(n_q * H, np.float32)
+    vis = np.full(n_q, n_k, np.int32)
+    lens = np.full(n_q, n_k, np.int32)
+    out = np.full(n_q * K, 7, np.int32)
+    ws = np.zeros(16, np.uint8)
+
+    def al(a):
+        return a.ctypes.data + (-a.ctypes.data) % 16
+
+    base = dict(q=al(q), qd=1, k=al(k), kd=1, w=_p(w), vis=_p(vis), n_q=n_q, mv=n_k, K=K,
+                oi=_p(out), cl=_p(lens), S=4, keep=K - 4, B=4, wsp=_p(ws), wsb=16)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.idx_score_topk_witness(a["q"], a["qd"], a["k"], a["kd"], None, a["w"], H, None,
+                                        a["vis"], a["n_q"], H, D, n_k, a["mv"], a["K"], a["oi"],
+                                        None, a["cl"], a["S"], a["keep"], a["B"], a["wsp"],
+                                        a["wsb"], None)
+
+    assert call(n_q=-1) == INVALID
+    assert call(keep=-1) == INVALID
+    assert call(B=-1) == INVALID
+    assert call(cl=None) == ROWS_MISMATCH
+    assert call(cl=None, S=65) == ROWS_MISMATCH  # the merge's order
+    assert call(oi=None, S=65) == INVALID
+    assert call(S=65) == SEGS
+    assert call(S=-1) == SEGS
+    assert call(keep=K + 1) == KEEP
+    assert call(S=4, q=None) == INVALID  # then the indexer's
+    assert call(kd=3) == DTYPE
+    assert call(K=4097, keep=0) == INVALID
+    assert call(cl=al(lens) + 2) == INVALID  # misaligned lengths
+    assert call() == WS
+    # the off switch and a zero budget: idx_score_topk's checks and result
+    assert call(S=0) == WS
+    assert call(keep=K) == WS
+    assert call(B=0, kd=3) == DTYPE
+    assert call(n_q=0) == OK
+    np.testing.assert_array_equal(out, 7)
+
+
 def test_idx_score_topk_prior_refusals(L):
     n_q, H, D, n_k, K, P = 4, 64, 128, 100, 16, 16
     q = np.zeros(n_q * H * D + 8, np.uint16)

@@ -1,0 +1,85 @@
+"""GPU parity of idx_score_topk_witness (the witness merge done by the top-K
+kernel as it writes each row): bit-identical to idx_score_topk followed by
+kvwitness_merge, which the witness tests pin to the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import dev_inputs, full_config, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(d, cfg, lens, S, keep, B, K=None, max_vis=None):
+    import sparse_attention_indexer_02_amd as si
+    K = K or cfg["topk"]
+    mv = max_vis or cfg["max_vis"]
+    kw = dict(k_scale=d["k_scale"], k_row_offset=d["k_row_offset"], max_vis=mv)
+    ui, us = si.idx_score_topk(d["q"], d["k"], d["w"], d["vis_len"], K, **kw)
+    si.kvwitness_merge(ui, lens, S, keep, B)
+    fi, fs = si.idx_score_topk_witness(d["q"], d["k"], d["w"], d["vis_len"], K, lens, S,
+                                       keep=keep, max_replacements=B, **kw)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(fi.cpu().numpy(), ui.cpu().numpy())
+    np.testing.assert_array_equal(fs.cpu().numpy().view(np.uint32), us.cpu().numpy().view(np.uint32))
+    return fi.cpu().numpy()
+
+
+def _lens(d, shift=0):
+    v = d["vis_len"].clone()
+    return (v + shift).contiguous()
+
+
+@pytest.mark.parametrize("S", [1, 4, 16, 64])
+def test_fused_prefill_small(S):
+    cfg = synth.prefill(seed=S, n_q=96, L=700, H=64, D=128, topk=128, S=S)
+    d = dev_inputs(cfg)
+    say(f"fused witness prefill S={S}")
+    K = cfg["topk"]
+    _both(d, cfg, _lens(d), S, max(K - S, 0), S)
+    _both(d, cfg, _lens(d), S, 0, 7)        # witnesses at the front of the row
+    _both(d, cfg, _lens(d), S, K - 2, 100)  # budget clipped to K - keep
+
+
+def test_fused_decode_levels():
+    """fp8 per-row keys with rows past 8192 (chunk levels; the merge runs in
+    the last one)."""
+    cfg = synth.decode(seed=3, rows=10, max_len=30000, topk=512)
+    d = dev_inputs(cfg)
+    say("fused witness decode levels")
+    _both(d, cfg, _lens(d), 64, 512 - 64, 64)
+
+
+def test_fused_context_lengths_differ():
+    """Context lengths unlike the visible lengths: ids past L (the clamped
+    segment rule), rows with no context, and rows that see no key but have a
+    context (every segment takes its witness)."""
+    cfg = synth.decode(seed=4, rows=12, max_len=3000, topk=256)
+    d = dev_inputs(cfg)
+    lens = d["vis_len"].clone()
+    lens[0] = 0
+    lens[1] = -3
+    lens[2] = 5
+    lens[3] = lens[3] // 3
+    lens[4] = lens[4] + 1000
+    d["vis_len"][5] = 0  # sees nothing, context kept
+    say("fused witness context lengths")
+    _both(d, cfg, lens.contiguous(), 16, 240, 16)
+
+
+def test_fused_large_k():
+    """K above the block kernel's 2048: radix-select rows, then the merge
+    kernel."""
+    cfg = synth.decode(seed=5, rows=6, max_len=9000, topk=3000)
+    d = dev_inputs(cfg)
+    say("fused witness K 3000")
+    _both(d, cfg, _lens(d), 32, 3000 - 32, 32)
+
+
+def test_fused_full_prefill():
+    cfg = full_config("prefill")
+    d = dev_inputs(cfg)
+    w = cfg["witness"]
+    say("fused witness full prefill")
+    _both(d, cfg, _lens(d), w["S"], w["keep"], w["max_rep"])
