@@ -111,6 +111,9 @@ struct TopkSmem {
 
 // One row (or one chunk of a row) with the kBT threads of the calling
 // workgroup; every thread must call it (it synchronises the workgroup).
+// WIT: the build with the fused witness merge (its extra state costs the
+// plain build's register budget, so the plain build leaves it out)
+template <bool WIT>
 __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy, TopkSmem& S) {
   BlockSmem& sm = S.sm;
   int* red = S.red;
@@ -147,7 +150,7 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   const int32_t* idmap = a.id_map ? a.id_map + (int64_t)r * a.id_map_stride + start : nullptr;
   // fused witness merge of a final row: the segment bits of the ids
   // written, OR-reduced once the row is out
-  const bool wit = a.wit_lens != nullptr && a.chunk == 0;
+  const bool wit = WIT && a.wit_lens != nullptr && a.chunk == 0;
   const int32_t wL = wit ? a.wit_lens[r] : 0;
   const uint32_t wS = (uint32_t)a.wit_S;
   const uint32_t wSe = wL > 0 ? (wS < (uint32_t)wL ? wS : (uint32_t)wL) : 0u;
@@ -510,7 +513,7 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
     const int32_t id = idmap ? idmap[p] : (int32_t)(start + p);
     oi[slot] = id;
     if (os) os[slot] = key_to_float((uint32_t)(c >> 32));
-    if (wL > 0) occ |= seg_bit(id, (uint32_t)wL, wS, wSe, wrcp);
+    if (WIT && wL > 0) occ |= seg_bit(id, (uint32_t)wL, wS, wSe, wrcp);
   };
   if (crowd <= (uint32_t)kCrowd) {
 #pragma unroll
