@@ -229,8 +229,8 @@ struct TopkArgs {
   size_t workspace_bytes = 0;
 };
 // Top-K of each row.  Rows of at most 8192 scores with K <= 2048 take one
-// workgroup each; longer rows are cut into 8192-score chunks whose ordered
-// top-K lists are selected from again (needs topk_workspace_bytes of
+// workgroup each; longer rows are cut into 8192-score chunks whose top-K
+// sets (in id order) are selected from again (needs topk_workspace_bytes of
 // workspace; without it, or for K > 2048, a single-workgroup radix select).
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 // The one-workgroup block top-K's limits (rows of at most this many scores,

@@ -6,9 +6,9 @@
 //  * topk_block: rows of at most 8192 scores, K <= 2048, one 512-thread
 //    workgroup per row holding the row in registers (steps in
 //    topk_block.hpp).  Longer rows (K <= 2048, with a workspace) are cut
-//    into 8192-score chunks whose ordered top-K lists, with the chunks'
-//    position maps, are selected from again by the same kernel until one
-//    chunk remains (each level's row lengths follow from the original ones,
+//    into 8192-score chunks whose top-K sets (in ascending position, so in
+//    id order), with the chunks' position maps, are selected from again by
+//    the same kernel until one chunk remains, which is ordered (each level's row lengths follow from the original ones,
 //    TopkArgs::len_levels).
 //  * topk_rows: K > 2048, or a long row without a workspace.  One
 //    512-thread workgroup per row; rows up to 8192 scores are staged in LDS,
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkArgs a) {
 }
 
 // eight waves per SIMD (64 VGPRs): four rows' 32 waves fill a CU
-template <bool WIT>
+template <bool WIT, bool CHUNK>
 __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(8))) void topk_block(
     TopkArgs a) {
   __shared__ TopkSmem S;
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(8))) void t
   } else {
     r = a.n_rows - 1 - r;  // causal rows grow with the index: longest first
   }
-  topk_row_block<WIT>(a, r, (int)blockIdx.y, S);
+  topk_row_block<WIT, CHUNK>(a, r, (int)blockIdx.y, S);
 }
 
 // Bytes of one chunk level (candidate ids + scores + per-row counts), and
@@ -126,8 +126,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.n_rows == 0) return hipSuccess;
   const dim3 grid((unsigned)a.n_rows);
   if (a.K <= kBK && a.max_vis <= kBN) {
-    if (a.wit_lens) hipLaunchKernelGGL(topk_block<true>, grid, dim3(kBT), 0, st, a);
-    else hipLaunchKernelGGL(topk_block<false>, grid, dim3(kBT), 0, st, a);
+    if (a.wit_lens) hipLaunchKernelGGL((topk_block<true, false>), grid, dim3(kBT), 0, st, a);
+    else hipLaunchKernelGGL((topk_block<false, false>), grid, dim3(kBT), 0, st, a);
     return hipGetLastError();
   }
   const size_t need = topk_workspace_bytes(a.n_rows, a.max_vis, a.K);
@@ -156,8 +156,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     L.out_idx = cidx;
     L.out_score = csc;
     L.out_stride = cstride;
-    hipLaunchKernelGGL(topk_block<false>, dim3((unsigned)a.n_rows, (unsigned)nch), dim3(kBT), 0, st,
-                       L);
+    hipLaunchKernelGGL((topk_block<false, true>), dim3((unsigned)a.n_rows, (unsigned)nch), dim3(kBT),
+                       0, st, L);
     // the next level's rows: the candidates this pass keeps, at the same
     // positions as the level's rows (lengths follow from the original ones)
     cur.scores = csc;
@@ -170,8 +170,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   }
   cur.out_idx = a.out_idx;
   cur.out_score = a.out_score;
-  if (a.wit_lens) hipLaunchKernelGGL(topk_block<true>, grid, dim3(kBT), 0, st, cur);
-  else hipLaunchKernelGGL(topk_block<false>, grid, dim3(kBT), 0, st, cur);
+  if (a.wit_lens) hipLaunchKernelGGL((topk_block<true, false>), grid, dim3(kBT), 0, st, cur);
+  else hipLaunchKernelGGL((topk_block<false, false>), grid, dim3(kBT), 0, st, cur);
   return hipGetLastError();
 }
 

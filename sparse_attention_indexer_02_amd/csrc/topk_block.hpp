@@ -112,8 +112,10 @@ struct TopkSmem {
 // One row (or one chunk of a row) with the kBT threads of the calling
 // workgroup; every thread must call it (it synchronises the workgroup).
 // WIT: the build with the fused witness merge (its extra state costs the
-// plain build's register budget, so the plain build leaves it out)
-template <bool WIT>
+// plain build's register budget, so the plain build leaves it out).
+// CHUNK: the build for chunk passes (a.chunk > 0), which end after the
+// selection; the final pass (a.chunk == 0) takes CHUNK false.
+template <bool WIT, bool CHUNK>
 __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy, TopkSmem& S) {
   BlockSmem& sm = S.sm;
   int* red = S.red;
@@ -132,7 +134,8 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   }
   const int K = a.K;
   // chunk mode: this block takes positions [start, start + chunk) of the row
-  // and writes its ordered top-K at y K of the output row; an empty chunk
+  // and writes its top-K set, in ascending position, at y K of the output
+  // row; an empty chunk
   // writes nothing (the next level never reads it)
   const int64_t start = a.chunk > 0 ? (int64_t)cy * a.chunk : 0;
   if (a.chunk > 0) {
@@ -462,6 +465,40 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
       selm = gtm | keep;
       __syncthreads();  // the bitmap area is reused by the scatter
     }
+  }
+
+  // E'. a chunk pass: the selected set in ascending position order, with
+  //    no order by score (only the last level orders).  A level's row is
+  //    its chunks' lists back to back, each in ascending position, so
+  //    position order is id order on every level, and the index-order tie
+  //    break at T stays exact.  Slot = the items of lower group rows, plus
+  //    those of lower threads in this group row, plus the lower lanes of
+  //    this thread's float4: one block scan of the four per-group counts,
+  //    packed 16 bits each (a group row holds at most 2048).
+  if (CHUNK) {
+    static_assert(kBGroups == 4, "four group rows, two packed counts per scan word");
+    auto gcount = [&](int j) { return __builtin_popcount((selm >> (4 * j)) & 0xFu); };
+    int tot01, tot23;
+    const int p01 = block_excl_scan<kBT>(gcount(0) | (gcount(1) << 16), red, &tot01);
+    const int p23 = block_excl_scan<kBT>(gcount(2) | (gcount(3) << 16), red, &tot23);
+    const int t0 = tot01 & 0xFFFF, t1 = tot01 >> 16, t2 = tot23 & 0xFFFF;
+    const int gbase[4] = {p01 & 0xFFFF, t0 + (p01 >> 16), t0 + t1 + (p23 & 0xFFFF),
+                          t0 + t1 + t2 + (p23 >> 16)};
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) {
+      if ((selm >> i) & 1u) {
+        const int slot =
+            gbase[i >> 2] + __builtin_popcount((selm >> (i & ~3)) & ((1u << (i & 3)) - 1u));
+        const int p = pos_of(i);
+        oi[slot] = idmap ? idmap[p] : (int32_t)(start + p);
+        if (os) os[slot] = x[i];
+      }
+    }
+    for (int q = cnt + t; q < K; q += kBT) {
+      oi[q] = -1;
+      if (os) os[q] = -__builtin_inff();
+    }
+    return;
   }
 
   // F. scatter the selected items grouped by bin (cursor = packed high
