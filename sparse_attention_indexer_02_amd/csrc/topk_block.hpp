@@ -261,6 +261,44 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
     vhi = __builtin_fmaxf(vhi, fred[1][i]);
   }
 
+  // Output of a chunk pass (after E, or at once when the chunk keeps
+  //    everything): the selected set in ascending position order, with
+  //    no order by score (only the last level orders).  A level's row is
+  //    its chunks' lists back to back, each in ascending position, so
+  //    position order is id order on every level, and the index-order tie
+  //    break at T stays exact.  Slot = the items of lower group rows, plus
+  //    those of lower threads in this group row, plus the lower lanes of
+  //    this thread's float4: one block scan of the four per-group counts,
+  //    packed 16 bits each (a group row holds at most 2048).
+  auto chunk_out = [&](const uint32_t selm) {
+    static_assert(kBGroups == 4, "four group rows, two packed counts per scan word");
+    auto gcount = [&](int j) { return __builtin_popcount((selm >> (4 * j)) & 0xFu); };
+    int tot01, tot23;
+    const int p01 = block_excl_scan<kBT>(gcount(0) | (gcount(1) << 16), red, &tot01);
+    const int p23 = block_excl_scan<kBT>(gcount(2) | (gcount(3) << 16), red, &tot23);
+    const int t0 = tot01 & 0xFFFF, t1 = tot01 >> 16, t2 = tot23 & 0xFFFF;
+    const int gbase[4] = {p01 & 0xFFFF, t0 + (p01 >> 16), t0 + t1 + (p23 & 0xFFFF),
+                          t0 + t1 + t2 + (p23 >> 16)};
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) {
+      if ((selm >> i) & 1u) {
+        const int slot =
+            gbase[i >> 2] + __builtin_popcount((selm >> (i & ~3)) & ((1u << (i & 3)) - 1u));
+        const int p = pos_of(i);
+        oi[slot] = idmap ? idmap[p] : (int32_t)(start + p);
+        if (os) os[slot] = x[i];
+      }
+    }
+    for (int q = cnt + t; q < K; q += kBT) {
+      oi[q] = -1;
+      if (os) os[q] = -__builtin_inff();
+    }
+  };
+  if (CHUNK && !select) {  // a short chunk keeps all of it: no threshold
+    chunk_out(vm);
+    return;
+  }
+
   // B. histogram over kBins bins linear in score value over [vmin, vmax]:
   //    bin(v) = (v - vmin) * scale rounded down, scale = (kBins - 0.01) /
   //    (vmax - vmin), so bin(vmax) < kBins after rounding.  bin() is
@@ -332,7 +370,9 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
     ab1 = red[kBT / 64 + 1];
     in_bin = red[kBT / 64 + 2];
     // selected counts: all of every bin above b1, want - ab1 of b1; output
-    // offsets are the exclusive prefix from the top
+    // offsets are the exclusive prefix from the top (the ordering phases'
+    // input: a chunk pass has none)
+    if (!CHUNK) {
     uint32_t o = (uint32_t)ab, crowd = 0u;
 #pragma unroll
     for (int j = 0; j < kBinsPer; ++j) {
@@ -349,9 +389,10 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
           make_uint4(c[4 * v + 3], c[4 * v + 2], c[4 * v + 1], c[4 * v + 0]);
     crowd = __ockl_wfred_max_u32(crowd);
     if (lane == 0) atomicMax(&S.crowd, crowd);
+    }
   }
   __syncthreads();
-  const uint32_t crowd = S.crowd;
+  const uint32_t crowd = CHUNK ? 0u : S.crowd;
 
   // D. the exact threshold value T inside b1
   float thr = 0.0f;
@@ -467,37 +508,8 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
     }
   }
 
-  // E'. a chunk pass: the selected set in ascending position order, with
-  //    no order by score (only the last level orders).  A level's row is
-  //    its chunks' lists back to back, each in ascending position, so
-  //    position order is id order on every level, and the index-order tie
-  //    break at T stays exact.  Slot = the items of lower group rows, plus
-  //    those of lower threads in this group row, plus the lower lanes of
-  //    this thread's float4: one block scan of the four per-group counts,
-  //    packed 16 bits each (a group row holds at most 2048).
   if (CHUNK) {
-    static_assert(kBGroups == 4, "four group rows, two packed counts per scan word");
-    auto gcount = [&](int j) { return __builtin_popcount((selm >> (4 * j)) & 0xFu); };
-    int tot01, tot23;
-    const int p01 = block_excl_scan<kBT>(gcount(0) | (gcount(1) << 16), red, &tot01);
-    const int p23 = block_excl_scan<kBT>(gcount(2) | (gcount(3) << 16), red, &tot23);
-    const int t0 = tot01 & 0xFFFF, t1 = tot01 >> 16, t2 = tot23 & 0xFFFF;
-    const int gbase[4] = {p01 & 0xFFFF, t0 + (p01 >> 16), t0 + t1 + (p23 & 0xFFFF),
-                          t0 + t1 + t2 + (p23 >> 16)};
-#pragma unroll
-    for (int i = 0; i < kBPer; ++i) {
-      if ((selm >> i) & 1u) {
-        const int slot =
-            gbase[i >> 2] + __builtin_popcount((selm >> (i & ~3)) & ((1u << (i & 3)) - 1u));
-        const int p = pos_of(i);
-        oi[slot] = idmap ? idmap[p] : (int32_t)(start + p);
-        if (os) os[slot] = x[i];
-      }
-    }
-    for (int q = cnt + t; q < K; q += kBT) {
-      oi[q] = -1;
-      if (os) os[q] = -__builtin_inff();
-    }
+    chunk_out(selm);
     return;
   }
 
