@@ -75,3 +75,18 @@ def test_long_rows(orc, kind):
     say(f"topk long {kind}")
     _check(orc, scores, vis, 2048)
     _check(orc, scores, vis, 4096)
+
+
+@pytest.mark.parametrize("kind", ["equal", "signed_zero", "narrow", "nan_inf", "bits"])
+@pytest.mark.parametrize("K", [1, 100, 2048])
+def test_deep_rows(orc, kind, K):
+    """Rows with three chunk levels (140000 scores: 18 chunks, then 5, then
+    2, then the last pass), ties spanning chunks and levels: chunk passes
+    keep their sets in position order, so the index tie-break must come out
+    exact at the last level."""
+    rng = np.random.default_rng(K + 7)
+    L = 140000
+    scores = _rows(kind, rng, 4, L)
+    vis = np.array([L, 8192 * 3 + 5, 16385, 9000])
+    say(f"topk deep {kind} K={K}")
+    _check(orc, scores, vis, K)
