@@ -83,3 +83,13 @@ def test_fused_full_prefill():
     w = cfg["witness"]
     say("fused witness full prefill")
     _both(d, cfg, _lens(d), w["S"], w["keep"], w["max_rep"])
+
+
+def test_fused_full_decode():
+    """The decode workload as timed: fp8 per-row keys, rows up to 131072
+    (chunk levels), K2048, S64."""
+    cfg = full_config("decode")
+    d = dev_inputs(cfg)
+    w = cfg["witness"]
+    say("fused witness full decode")
+    _both(d, cfg, _lens(d), w["S"], w["keep"], w["max_rep"])
