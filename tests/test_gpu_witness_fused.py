@@ -93,3 +93,14 @@ def test_fused_full_decode():
     w = cfg["witness"]
     say("fused witness full decode")
     _both(d, cfg, _lens(d), w["S"], w["keep"], w["max_rep"])
+
+
+@pytest.mark.parametrize("S,keep,B", [(64, 100, 3), (64, 0, 64), (7, 120, 8), (1, 127, 1)])
+def test_fused_budgets(S, keep, B):
+    """Budgets below the empty-segment count (only the first B witnesses in
+    segment order), keep far below topk - S, keep 0, and a budget past the
+    row's tail (clipped to topk - keep)."""
+    cfg = synth.prefill(seed=S + keep, n_q=64, L=900, H=64, D=128, topk=128, S=S)
+    d = dev_inputs(cfg)
+    say(f"fused witness budgets S={S} keep={keep} B={B}")
+    _both(d, cfg, _lens(d), S, keep, B)
