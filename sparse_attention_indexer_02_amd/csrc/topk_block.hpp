@@ -32,6 +32,12 @@ namespace si {
 //     that slot of the output row.  If some bin holds more than kCrowd
 //     selected items (heavy ties, very uneven scores) the row is ordered by
 //     a bitonic sort in LDS and written from there.
+// A chunk pass (CHUNK) needs the set, not its order: after the selection it
+// writes the selected items in ascending position and stops (C skips the
+// per-bin offsets; a chunk with at most K items skips B to D).  The final
+// pass of a fused witness merge (WIT) also ORs each written id's segment
+// bit into the row's occupancy and, once the row is out, writes the
+// witnesses of the empty segments.
 // Staged items are 64-bit composites: order key << 32 | bin << 13 |
 // (8191 - position); composites compare as (score desc, index asc), and the
 // bin rides along so the rank step need not recompute it.
