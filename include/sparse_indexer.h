@@ -309,8 +309,9 @@ si_status kvwitness_merge(int32_t* topk_idx, int32_t rows, int32_t topk,
 /* ------------------------------------------------------------------------ *
  * block_sparse_select
  *
- * ferrox_core block_sparse.rs (docs.rs, ferrox-core 0.14.0), fns
- * block_sparse_select / select_for_head / dot.  For query i at position
+ * ferrox_core block_sparse.rs (docs.rs, ferrox-core 0.14.0): module docs
+ * "Four rules", the public selection entry's doc comment and the per-head
+ * selection's comments on scoring and ties.  For query i at position
  * p = query_pos[i]: n_blocks = min(p / block_size + 1, ceil(n_pos /
  * block_size)) (0 when p < 0).  Per KV head h independently: the first
  * min(init_blocks, n) and the last min(local_blocks, n) blocks are forced;
@@ -342,8 +343,9 @@ size_t block_sparse_select_workspace(int32_t n_q, int32_t n_kv_heads, int64_t n_
 /* ------------------------------------------------------------------------ *
  * positions_of_blocks
  *
- * ferrox_core block_sparse.rs (docs.rs, ferrox-core 0.14.0), fn
- * positions_of_blocks: the positions a block list covers, ascending and
+ * ferrox_core block_sparse.rs (docs.rs, ferrox-core 0.14.0), the
+ * positions helper's doc comment: the positions a block list covers,
+ * ascending and
  * deduplicated, each block b covering [b*bs, min((b+1)*bs, n_pos, p+1))
  * for the query at p = query_pos[i] (nothing when p < 0).  Negative entries
  * are padding and cover nothing; the list may be in any order and repeat

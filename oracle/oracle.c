@@ -336,9 +336,11 @@ double orc_segment_coverage(const int32_t* cand, int32_t n, int64_t L, int64_t n
 /* Block-sparse selection ([BLOCK])                                           */
 /* ------------------------------------------------------------------------ */
 
-/* [BLOCK] fn dot: the f32 sum, in index order, of f32 products.  Each
- * product is rounded to f32 and then added (no fused multiply-add); the sum
- * starts at +0.0f, so the result is never -0. */
+/* [BLOCK] module docs, "Four rules": a block is scored by the raw dot
+ * product of the index query and a position's index key, with no scale.  The
+ * page's dot helper sums f32 products in index order: each product is rounded
+ * to f32 and then added (no fused multiply-add), starting from +0.0f, so the
+ * result is never -0. */
 float orc_block_dot(const float* a, const float* b, int32_t D) {
   float acc = 0.0f;
   for (int32_t d = 0; d < D; ++d) {
@@ -348,96 +350,95 @@ float orc_block_dot(const float* a, const float* b, int32_t D) {
   return acc;
 }
 
-/* [BLOCK] causal_blocks: blocks covering positions 0..=query_pos; 0 when the
- * block size is 0.  A negative position sees no block. */
+/* [BLOCK] the configuration's causal block count: the blocks covering
+ * positions 0..=query_pos; 0 when the block size is 0.  A negative position
+ * sees no block. */
 int64_t orc_causal_blocks(int64_t query_pos, int64_t block_size) {
   if (block_size <= 0 || query_pos < 0) return 0;
   return query_pos / block_size + 1;
 }
 
-typedef struct {
-  float s;
-  int32_t b;
-} scored_block;
-
-/* [BLOCK] select_for_head sort: score descending under the total order, ties
- * toward the lower block.  Scores here are never NaN and never -0, where the
- * IEEE comparison and the total order agree. */
-static int cmp_block(const void* pa, const void* pb) {
-  const scored_block* a = (const scored_block*)pa;
-  const scored_block* b = (const scored_block*)pb;
-  if (a->s > b->s) return -1;
-  if (a->s < b->s) return 1;
-  return (a->b > b->b) - (a->b < b->b);
+/* [BLOCK] the order of block scores: higher score first; equal scores go to
+ * the lower block (the selection's comment on deterministic ties).  Scores
+ * are never NaN and never -0 here, where the IEEE comparison is the page's
+ * total order. */
+static int block_before(float sa, int64_t a, float sb, int64_t b) {
+  return sa > sb || (sa == sb && a < b);
 }
 
-static int cmp_i32(const void* pa, const void* pb) {
-  int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
-  return (a > b) - (a < b);
-}
-
-/* [BLOCK] block_sparse_select + select_for_head, for one query position.
- * Returns 0, or -1 if `width` cannot hold a selection. */
+/* [BLOCK] the public selection entry's doc comment and the module docs
+ * ("Four rules"), for one query position, stated as a set:
+ *   n   = min(causal blocks, ceil(n_pos / bs))   (a query cannot see past
+ *         the keys that exist); n == 0 gives empty selections;
+ *   F   = the first min(init, n) blocks and the last min(local, n) blocks,
+ *         force-included before any scoring;
+ *   B   = max(top, |F|), the budget counting the forced blocks;
+ *   per KV head h, every other block b gets score(b) = the MAX over its
+ *         causally visible positions [b bs, min((b+1) bs, n_pos, pos+1)) of
+ *         the dot above;
+ *   the selection is F plus the non-forced blocks whose rank under the
+ *         order above is below B - |F| (a block's rank = the number of
+ *         non-forced blocks ordered before it), written ascending.
+ * Its size is min(n, B).  Returns 0, or -1 if `width` cannot hold a
+ * selection. */
 int32_t orc_block_select_query(const float* q, const float* k, int64_t query_pos, int32_t H,
                                int32_t D, int64_t n_pos, int32_t block_size, int32_t top_blocks,
                                int32_t init_blocks, int32_t local_blocks, int32_t* out,
                                int32_t width, int32_t* counts, float* block_scores) {
-  int64_t n_blocks = orc_causal_blocks(query_pos, block_size);
+  int64_t n = orc_causal_blocks(query_pos, block_size);
   int64_t exist = block_size > 0 ? (n_pos + block_size - 1) / block_size : 0;
-  if (exist < n_blocks) n_blocks = exist; /* a query cannot see past the keys */
+  if (exist < n) n = exist;
   for (int32_t h = 0; h < H; ++h) {
     counts[h] = 0;
     for (int32_t t = 0; t < width; ++t) out[(int64_t)h * width + t] = -1;
   }
-  if (n_blocks <= 0) return 0;
-  unsigned char* forced = (unsigned char*)calloc((size_t)n_blocks, 1);
-  int32_t* chosen = (int32_t*)malloc(sizeof(int32_t) * n_blocks);
-  scored_block* sc = (scored_block*)malloc(sizeof(scored_block) * n_blocks);
-  int64_t n_init = init_blocks < n_blocks ? init_blocks : n_blocks;
-  int64_t local_start = n_blocks > local_blocks ? n_blocks - local_blocks : 0; /* saturating */
-  for (int64_t b = 0; b < n_init; ++b) forced[b] = 1;
-  for (int64_t b = local_start; b < n_blocks; ++b) forced[b] = 1;
+  if (n <= 0) return 0;
+  unsigned char* forced = (unsigned char*)calloc((size_t)n, 1);
+  float* score = (float*)malloc(sizeof(float) * (size_t)n);
+  for (int64_t b = 0; b < n; ++b)
+    forced[b] = (b < init_blocks) || (b >= n - local_blocks);
   int64_t nf = 0;
-  for (int64_t b = 0; b < n_blocks; ++b) nf += forced[b];
-  int64_t budget = top_blocks > nf ? top_blocks : nf;
+  for (int64_t b = 0; b < n; ++b) nf += forced[b];
+  const int64_t budget = top_blocks > nf ? top_blocks : nf;
+  const int64_t free_slots = budget - nf; /* non-forced blocks that join */
   int32_t rc = 0;
   for (int32_t h = 0; h < H && rc == 0; ++h) {
     const float* qh = q + (int64_t)h * D;
-    int64_t nc = 0;
-    for (int64_t b = 0; b < n_blocks; ++b)
-      if (forced[b]) chosen[nc++] = (int32_t)b;
-    if (!(nc >= budget || nc == n_blocks)) {
-      int64_t ns = 0;
-      for (int64_t b = 0; b < n_blocks; ++b) {
+    if (free_slots > 0) {
+      for (int64_t b = 0; b < n; ++b) {
         if (forced[b]) continue;
-        int64_t start = b * block_size;
         int64_t end = (b + 1) * block_size;
         if (end > n_pos) end = n_pos;
         if (end > query_pos + 1) end = query_pos + 1;
-        float best = -INFINITY; /* MAX over the block's visible positions */
-        for (int64_t p = start; p < end; ++p) {
+        float best = -INFINITY;
+        for (int64_t p = b * block_size; p < end; ++p) {
           float v = orc_block_dot(qh, k + p * D, D);
           if (v > best) best = v;
         }
-        if (block_scores) block_scores[(int64_t)h * n_blocks + b] = best;
-        sc[ns].s = best;
-        sc[ns].b = (int32_t)b;
-        ++ns;
+        score[b] = best;
+        if (block_scores) block_scores[(int64_t)h * n + b] = best;
       }
-      qsort(sc, (size_t)ns, sizeof(scored_block), cmp_block);
-      for (int64_t t = 0; t < ns && nc < budget; ++t) chosen[nc++] = sc[t].b;
     }
-    qsort(chosen, (size_t)nc, sizeof(int32_t), cmp_i32);
-    if (nc > width) {
-      rc = -1;
-      break;
+    int64_t c = 0;
+    for (int64_t b = 0; b < n; ++b) {
+      int in = forced[b];
+      if (!in && free_slots > 0) {
+        int64_t rank = 0;
+        for (int64_t o = 0; o < n && rank < free_slots; ++o)
+          if (!forced[o] && block_before(score[o], o, score[b], b)) ++rank;
+        in = rank < free_slots;
+      }
+      if (!in) continue;
+      if (c >= width) {
+        rc = -1;
+        break;
+      }
+      out[(int64_t)h * width + c++] = (int32_t)b;
     }
-    for (int64_t t = 0; t < nc; ++t) out[(int64_t)h * width + t] = chosen[t];
-    counts[h] = (int32_t)nc;
+    counts[h] = (int32_t)c;
   }
   free(forced);
-  free(chosen);
-  free(sc);
+  free(score);
   return rc;
 }
 
@@ -455,8 +456,8 @@ void orc_block_select_rows(const float* q, const float* k, const int64_t* query_
   }
 }
 
-/* [BLOCK] positions_of_blocks: covered positions, ascending, causally
- * clipped, deduplicated.  Returns the count written to out.  A negative
+/* [BLOCK] the doc comment of the positions helper: the positions a block
+ * selection covers, ascending, causally clipped, deduplicated.  Returns the count written to out.  A negative
  * entry is the -1 padding of an i32 block list and covers nothing (the
  * page's lists are unsigned and unpadded). */
 int64_t orc_positions_of_blocks(const int32_t* blocks, int32_t n_sel, int64_t query_pos,
@@ -540,6 +541,11 @@ void orc_gather_slots(const int32_t* idx, int32_t rows, int32_t width, const int
 /* ------------------------------------------------------------------------ */
 /* DoSA certified prune ([DoSA])                                              */
 /* ------------------------------------------------------------------------ */
+
+static int cmp_i32(const void* pa, const void* pb) {
+  int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+  return (a > b) - (a < b);
+}
 
 /* Seeds must be visible to every row: the common visible prefix [0, c). */
 int32_t orc_dosa_common_prefix(const orc_problem* P) {

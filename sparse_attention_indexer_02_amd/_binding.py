@@ -133,14 +133,25 @@ def _workspace(nbytes, dev, given):
     return torch.empty(nbytes, dtype=torch.uint8, device=dev), nbytes
 
 
+def _default_max_vis(n_k, k_row_offset, vis_len, n_q):
+    """max_vis when the caller gives none: n_k for shared keys; for per-row
+    keys the longest visible length, read back to the host (a device
+    synchronisation: callers that must not block pass max_vis)."""
+    if k_row_offset is None:
+        return n_k
+    return int(vis_len.max().item()) if n_q else 0
+
+
 def idx_score_topk(q, k, w, vis_len, topk, *, k_scale=None, k_row_offset=None, max_vis=None,
                    out_idx=None, out_score=None, want_scores=True, workspace=None):
     """Top-K of s = sum_h w_h relu(q_h . k) per row; returns (idx, scores|None).
 
     q [n_q, H, D] bf16/f32; k [n_k, D] bf16/f32/fp8-e4m3fn (uint8 storage ok)
     with k_scale [n_k] f32 for fp8; w [n_q, H] or [H] f32; vis_len [n_q] i32;
-    k_row_offset [n_q] i64 or None.  max_vis defaults to n_k for shared keys,
-    else to vis_len.max() (a host read).
+    k_row_offset [n_q] i64 or None.  max_vis defaults to n_k for shared keys.
+    With per-row keys and max_vis=None it is vis_len.max() read back to the
+    host, which synchronises the device (the library's calls never do): pass
+    max_vis to keep the call asynchronous.
     """
     _dev_tensor(q, "q")
     _dev_tensor(k, "k")
@@ -150,7 +161,7 @@ def idx_score_topk(q, k, w, vis_len, topk, *, k_scale=None, k_row_offset=None, m
     n_q, H, D = q.shape
     n_k = k.shape[0]
     if max_vis is None:
-        max_vis = n_k if k_row_offset is None else (int(vis_len.max().item()) if n_q else 0)
+        max_vis = _default_max_vis(n_k, k_row_offset, vis_len, n_q)
     w_stride = H if w.dim() == 2 else 0
     if out_idx is None:
         out_idx = torch.empty((n_q, topk), dtype=torch.int32, device=dev)
@@ -185,7 +196,7 @@ def idx_score_topk_witness(q, k, w, vis_len, topk, context_lens, num_segments, *
     if max_replacements is None:
         max_replacements = num_segments
     if max_vis is None:
-        max_vis = n_k if k_row_offset is None else (int(vis_len.max().item()) if n_q else 0)
+        max_vis = _default_max_vis(n_k, k_row_offset, vis_len, n_q)
     w_stride = H if w.dim() == 2 else 0
     if out_idx is None:
         out_idx = torch.empty((n_q, topk), dtype=torch.int32, device=dev)
@@ -219,7 +230,7 @@ def idx_score_topk_prior(q, k, w, vis_len, topk, prior_ids, *, k_scale=None, k_r
     n_q, H, D = q.shape
     n_k = k.shape[0]
     if max_vis is None:
-        max_vis = n_k if k_row_offset is None else (int(vis_len.max().item()) if n_q else 0)
+        max_vis = _default_max_vis(n_k, k_row_offset, vis_len, n_q)
     w_stride = H if w.dim() == 2 else 0
     if out_idx is None:
         out_idx = torch.empty((n_q, topk), dtype=torch.int32, device=dev)
@@ -252,7 +263,7 @@ def idx_score(q, k, w, vis_len, *, k_scale=None, k_row_offset=None, max_vis=None
     n_q, H, D = q.shape
     n_k = k.shape[0]
     if max_vis is None:
-        max_vis = n_k if k_row_offset is None else (int(vis_len.max().item()) if n_q else 0)
+        max_vis = _default_max_vis(n_k, k_row_offset, vis_len, n_q)
     if out_scores is None:
         out_scores = torch.empty((n_q, max_vis), dtype=torch.float32, device=dev)
     stride = out_scores.shape[1] if out_scores.dim() == 2 else max_vis

@@ -1,5 +1,7 @@
-// MiniMax-M3 block-sparse selection (ferrox_core block_sparse.rs:
-// block_sparse_select, select_for_head, dot).
+// MiniMax-M3 block-sparse selection (ferrox_core block_sparse.rs on
+// docs.rs, ferrox-core 0.14.0: module docs "Four rules", the public
+// selection entry's doc comment, and the per-head selection's comments on
+// scoring by the best position and on ties toward the lower block).
 //
 // Pass 1 (block_max): a block's score for (query, KV head) is the MAX over
 // the block's causally visible positions of the page's f32 dot - products

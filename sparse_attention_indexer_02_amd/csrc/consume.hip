@@ -2,7 +2,8 @@
 // selection reads.
 //
 //  * block_positions: the positions a block list covers (ferrox-core
-//    block_sparse.rs, positions_of_blocks): ascending, deduplicated, and
+//    block_sparse.rs, the positions helper's doc comment): ascending,
+//    deduplicated, and
 //    clipped to the keys that exist and to the query's own position.  Lists
 //    of at most 64 entries take one wave each (block_positions_wave, below);
 //    longer ones one 256-thread workgroup each.  A list's entries

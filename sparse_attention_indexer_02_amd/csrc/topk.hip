@@ -44,11 +44,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkArgs a) {
   const float* row = a.scores + (int64_t)r * a.stride;
   const int K = a.K;
   const bool staged = n <= kStage;
+  // a NaN score ranks (and is reported) as -inf, as in the block kernel;
+  // order_key folds -0 onto +0
+  auto key_at = [&](int64_t i) -> uint32_t {
+    const float v = row[i];
+    return order_key(v == v ? v : -__builtin_inff());
+  };
   if (staged)
-    for (int64_t i = threadIdx.x; i < n; i += T) keys[i] = order_key(row[i]);
+    for (int64_t i = threadIdx.x; i < n; i += T) keys[i] = key_at(i);
   if (threadIdx.x == 0) counter = 0;
   __syncthreads();
-  auto load = [&](int64_t i) -> uint32_t { return staged ? keys[i] : order_key(row[i]); };
+  auto load = [&](int64_t i) -> uint32_t { return staged ? keys[i] : key_at(i); };
 
   const int cnt = (int)(n < K ? n : K);
   const int P = next_pow2(cnt > 1 ? cnt : 1);

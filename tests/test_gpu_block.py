@@ -90,13 +90,22 @@ def test_minimax_geometry_medium(orc):
     np.testing.assert_array_equal(gc, wc)
 
 
-def test_full_size_sampled_queries(orc):
-    """4096 queries over 131072 positions, 8 KV heads, D = 128; queries sampled
-    for the oracle, including the last (which sees every position)."""
+def test_full_size_queries(orc):
+    """4096 queries over 131072 positions, 8 KV heads, D = 128.  Query j sits at
+    32 j + 31, so queries 4m + 3 end a 128-position block and queries 4m + 4
+    open the next one with 32 visible positions.  384 queries against the
+    oracle: both sides of 128 block boundaries spread over the range (the
+    partial newest block, the local pair shifting), the first 32 queries
+    (fewer blocks than the budget, forced blocks overlapping) and the last
+    one (every position visible)."""
     cfg = full_config("block")
     say("block full size")
     got, gc = _gpu_select(cfg["q"], cfg["k"], cfg["query_pos"], 128, 32, 1, 2)
-    rows = [0, 1, 3, 4, 35, 36, 1000, 2047, 4095]
+    m = np.linspace(0, 1022, 128).astype(np.int64)
+    rows = sorted(set(range(32)) | set((4 * m + 3).tolist()) | set((4 * m + 4).tolist()) |
+                  {4095})
+    rows = np.array(rows, np.int32)
+    say(f"block full size: {len(rows)} queries against the oracle")
     out, cnt = orc.block_select_rows(cfg, rows)
     np.testing.assert_array_equal(got[rows], out)
     np.testing.assert_array_equal(gc[rows], cnt)
@@ -104,3 +113,7 @@ def test_full_size_sampled_queries(orc):
     nb = np.minimum(cfg["query_pos"] // 128 + 1, 1024)
     assert np.all(gc == np.minimum(nb, 32)[:, None])
     assert np.all(got[:, :, 0] == 0)
+    sel = np.where(got >= 0, got, np.iinfo(np.int32).max)
+    assert np.all(np.diff(sel, axis=2)[got[:, :, 1:] >= 0] > 0)
+    last = np.take_along_axis(got, (gc - 1)[:, :, None], axis=2)[:, :, 0]
+    assert np.all(last == (nb - 1)[:, None])

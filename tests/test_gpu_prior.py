@@ -7,7 +7,7 @@ import torch
 
 import synth
 from gpu_util import dev_inputs, full_config, say
-from parity import check_topk_row
+from parity import oracle_check_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -125,21 +125,14 @@ def test_prior_overflow_rows(orc):
 
 def test_prior_full_size(orc):
     """128 ragged rows up to 131072 fp8 keys with a perturbed-query prior:
-    equal to idx_score_topk; sampled rows against the oracle."""
+    equal to idx_score_topk; every row against the oracle."""
     cfg = full_config("decode")
     d = dev_inputs(cfg)
     prior = _perturbed_prior(d, cfg, 0.3, 3)
     ui, us, surv = _check_equal(d, cfg, prior, "full-size decode, perturbed prior")
     say(f"survivors {int(surv.sum())} of {int(np.minimum(cfg['vis_len'], cfg['max_vis']).sum())}")
-    kp = orc.problem(cfg)
-    lens = cfg["vis_len"]
-    order = np.argsort(lens)
-    rows = sorted(set(order[-2:].tolist() + order[:1].tolist() + [9]))
-    oi, os_, S, M, N = orc.idx_score_topk_rows(kp, rows, want_rows=True)
-    for n, r in enumerate(rows):
-        v = orc.visible(kp, int(r))
-        check_topk_row(ui[r], us[r], S[n, :v], M[n, :v], N[n, :v], cfg["topk"],
-                       where=f"prior full-size row {r}")
+    ndiff = oracle_check_rows(orc, cfg, ui, us, chunk=32, where="prior full-size")
+    say(f"prior full size: every row against the oracle, {ndiff} differ within the near-K-th rule")
 
 
 @pytest.mark.parametrize("lens", [[0, 3000, 1, 9000], [0, 600000, 5000, 1]])

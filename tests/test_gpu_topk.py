@@ -66,9 +66,10 @@ def test_short_rows(orc, kind, L, K):
     _check(orc, scores, vis, K)
 
 
-@pytest.mark.parametrize("kind", ["normal", "few_values"])
+@pytest.mark.parametrize("kind", ["normal", "few_values", "nan_inf", "bits"])
 def test_long_rows(orc, kind):
-    """Rows longer than the register-resident path (up to 40000)."""
+    """Rows longer than the register-resident path (up to 40000); K = 4096
+    takes the radix-select kernel."""
     rng = np.random.default_rng(3)
     scores = _rows(kind, rng, 6, 40000)
     vis = np.array([40000, 8193, 12288, 20000, 2, 0])
@@ -89,4 +90,18 @@ def test_deep_rows(orc, kind, K):
     scores = _rows(kind, rng, 4, L)
     vis = np.array([L, 8192 * 3 + 5, 16385, 9000])
     say(f"topk deep {kind} K={K}")
+    _check(orc, scores, vis, K)
+
+
+@pytest.mark.parametrize("kind", ["normal", "signed_zero", "nan_inf", "bits"])
+@pytest.mark.parametrize("L,K", [(5000, 3000), (700, 4096), (8192, 2049)])
+def test_short_rows_large_k(orc, kind, L, K):
+    """K above the block kernel's 2048 on rows of at most 8192 scores: the
+    radix-select kernel with the row staged in LDS, including rows shorter
+    than K and non-finite scores (NaN ranks and is reported as -inf)."""
+    rng = np.random.default_rng(L + 3 * K)
+    scores = _rows(kind, rng, 12, L)
+    vis = rng.integers(0, L + 1, 12)
+    vis[:4] = [0, 1, min(K, L), L]
+    say(f"topk large K {kind} L={L} K={K}")
     _check(orc, scores, vis, K)

@@ -7,6 +7,7 @@ import torch
 
 import synth
 from gpu_util import dev_inputs, full_config, say
+from parity import oracle_check_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -77,15 +78,44 @@ def test_fused_large_k():
     _both(d, cfg, _lens(d), 32, 3000 - 32, 32)
 
 
-def test_fused_full_prefill():
+def _full_step_against_oracle(orc, name, chunk):
+    """The timed step, idx_score_topk_witness without scores, at full size:
+    its unmerged rows (idx_score_topk) are checked row by row against the
+    oracle, and the step's ids must equal the oracle's witness merge applied
+    to those same rows, bit for bit (both sides merge the same learned
+    rows)."""
+    import sparse_attention_indexer_02_amd as si
+    cfg = full_config(name)
+    d = dev_inputs(cfg)
+    w = cfg["witness"]
+    K, mv = cfg["topk"], cfg["max_vis"]
+    kw = dict(k_scale=d["k_scale"], k_row_offset=d["k_row_offset"], max_vis=mv)
+    say(f"fused witness full {name}: the timed call, then every row against the oracle")
+    ui, us = si.idx_score_topk(d["q"], d["k"], d["w"], d["vis_len"], K, **kw)
+    fi, _ = si.idx_score_topk_witness(d["q"], d["k"], d["w"], d["vis_len"], K, d["vis_len"],
+                                      w["S"], keep=w["keep"], max_replacements=w["max_rep"],
+                                      want_scores=False, **kw)
+    torch.cuda.synchronize()
+    ui, us, fi = ui.cpu().numpy(), us.cpu().numpy(), fi.cpu().numpy()
+    ndiff = oracle_check_rows(orc, cfg, ui, us, chunk=chunk, where=f"{name} full step")
+    rc, merged = orc.kvwitness_merge(ui, cfg["vis_len"], w["S"], w["keep"], w["max_rep"])
+    assert rc == 0
+    np.testing.assert_array_equal(fi, merged)
+    changed = int((fi != ui).sum())
+    say(f"{name}: {ndiff} rows differ from the oracle's top-K within the near-K-th rule; "
+        f"{changed} slots hold witnesses")
+
+
+def test_fused_full_prefill(orc):
     cfg = full_config("prefill")
     d = dev_inputs(cfg)
     w = cfg["witness"]
     say("fused witness full prefill")
     _both(d, cfg, _lens(d), w["S"], w["keep"], w["max_rep"])
+    _full_step_against_oracle(orc, "prefill", 1024)
 
 
-def test_fused_full_decode():
+def test_fused_full_decode(orc):
     """The decode workload as timed: fp8 per-row keys, rows up to 131072
     (chunk levels), K2048, S64."""
     cfg = full_config("decode")
@@ -93,6 +123,7 @@ def test_fused_full_decode():
     w = cfg["witness"]
     say("fused witness full decode")
     _both(d, cfg, _lens(d), w["S"], w["keep"], w["max_rep"])
+    _full_step_against_oracle(orc, "decode", 32)
 
 
 @pytest.mark.parametrize("S,keep,B", [(64, 100, 3), (64, 0, 64), (7, 120, 8), (1, 127, 1)])

@@ -57,6 +57,43 @@ def test_score_unit_keys_pick_one_coordinate(orc):
         assert np.all(n >= m - 1e-12)  # Cauchy-Schwarz on every head
 
 
+def test_tolerance_scales_by_value(orc):
+    """The tolerance scales m = sum_h |w_h| max(0, x_h) and n = sum_h |w_h|
+    |q_h| |k| of the parity rule, pinned by value on hand-worked integer
+    cases (the score itself is the one of the DoSA notes, section 3).
+    Heads q_0 = (3, 4) with |q_0| = 5 and q_1 = (-6, 8) with |q_1| = 10,
+    weights 2 and -1/2, so sum_h |w_h| |q_h| = 2*5 + 5 = 15:
+      k = (1, 0):  x = (3, -6)    s = 6     m = 6             n = 15
+      k = (0, 2):  x = (8, 16)    s = 16-8  m = 16+8 = 24     n = 15*2 = 30
+      k = (3, -4): x = (-7, -50)  s = 0     m = 0             n = 15*5 = 75
+      k = (-3, 4): x = (7, 50)    s = 14-25 m = 14+25 = 39    n = 75
+    A signed weight in m (m = -11 on the last key), a dropped |w_h| in n
+    (n = 10 - 5 = 5 on the first), 1-norms of q (n = 2*7 + 14/2 = 21) or of
+    k (n = 15*7 = 105 on the third) all miss these values."""
+    q = np.array([[[3.0, 4.0], [-6.0, 8.0]]], np.float32)
+    k = np.array([[1.0, 0.0], [0.0, 2.0], [3.0, -4.0], [-3.0, 4.0]], np.float32)
+    cfg = _cfg(q, k, [[2.0, -0.5]], [4])
+    s, m, n = orc.score_row(cfg, 0)
+    assert list(s) == [6.0, 8.0, 0.0, -11.0]
+    assert list(m) == [6.0, 24.0, 0.0, 39.0]
+    assert list(n) == [15.0, 30.0, 75.0, 75.0]
+
+
+def test_tolerance_scales_fp8_key_carries_its_scale(orc):
+    """n takes the norm of the dequantised key: e4m3fn bytes 0x44 = 3 and
+    0x48 = 4 with per-token scale 2 give k = (6, 8), |k| = 10.  With the heads
+    and weights above: x = (18 + 32, -36 + 64) = (50, 28), s = 100 - 14 = 86,
+    m = 100 + 14 = 114, n = 15 * 10 = 150 (75 if the scale were left out of
+    the norm)."""
+    assert orc.e4m3fn_to_double(0x44) == 3.0 and orc.e4m3fn_to_double(0x48) == 4.0
+    q = synth.f32_to_bf16_bits(np.array([[[3.0, 4.0], [-6.0, 8.0]]], np.float32))
+    kb = np.array([[0x44, 0x48]], np.uint8)
+    cfg = _cfg(q, kb, [[2.0, -0.5]], [1], q_dtype=1, k_dtype=2,
+               k_scale=np.array([2.0], np.float32))
+    s, m, n = orc.score_row(cfg, 0)
+    assert (s[0], m[0], n[0]) == (86.0, 114.0, 150.0)
+
+
 def test_score_positive_scale_commutes_with_relu(orc):
     """fp8 keys: the per-token scale c > 0 satisfies ReLU(c x) = c ReLU(x), so
     doubling every scale doubles every score exactly."""
