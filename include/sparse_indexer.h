@@ -58,7 +58,10 @@ typedef enum {
   SI_ERR_LEARNED_KEEP_OUT_OF_RANGE = 4,
   SI_ERR_UNSUPPORTED_DTYPE = 5,
   SI_ERR_WORKSPACE_TOO_SMALL = 6,
-  SI_ERR_DEVICE = 7
+  SI_ERR_DEVICE = 7,
+  /* idx_score_topk_noalloc: the problem needs more scratch than the
+   * library's fixed array holds (SI_NOALLOC_SCRATCH_BYTES) */
+  SI_ERR_SCRATCH_LIMIT = 8
 } si_status;
 
 typedef enum { SI_F32 = 0, SI_BF16 = 1, SI_FP8_E4M3FN = 2 } si_dtype;
@@ -109,6 +112,37 @@ si_status idx_score_topk(const void* q, si_dtype q_dtype, const void* k, si_dtyp
                          int32_t* out_idx, float* out_score, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 size_t idx_score_topk_workspace(int32_t n_q, int32_t H, int32_t D, int64_t max_vis, int32_t topk);
+
+/* ------------------------------------------------------------------------ *
+ * idx_score_topk_noalloc
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * call and result as idx_score_topk (bit for bit), without a workspace
+ * argument: the score rows and candidate lists live in a fixed array inside
+ * the library, SI_NOALLOC_SCRATCH_BYTES per GPU, allocated when the library
+ * is loaded on that GPU and held until the process ends.  The call itself
+ * allocates nothing; its first call on a GPU looks the array's address up
+ * once (a runtime query, no allocation).
+ * Limit: idx_score_topk_workspace(n_q, H, D, max_vis, topk) must be at most
+ * SI_NOALLOC_SCRATCH_BYTES (128 MiB: e.g. 4096 queries x 8192 keys, or 128
+ * decode rows of up to 131072 keys); a larger problem is refused with
+ * SI_ERR_SCRATCH_LIMIT before anything runs.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (several streams, several host threads) race and must be ordered by
+ * the caller.  The array keeps the last call's contents; nothing in it needs
+ * to start at zero.  The GPU is the device of `stream` (the current device
+ * for the null stream).
+ * Arguments and other errors as idx_score_topk; SI_ERR_DEVICE also when the
+ * array's address cannot be obtained.
+ * ------------------------------------------------------------------------ */
+#define SI_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+si_status idx_score_topk_noalloc(const void* q, si_dtype q_dtype, const void* k, si_dtype k_dtype,
+                                 const float* k_scale, const float* w, int64_t w_row_stride,
+                                 const int64_t* k_row_offset, const int32_t* vis_len,
+                                 int32_t n_q, int32_t H, int32_t D, int64_t n_k, int64_t max_vis,
+                                 int32_t topk, int32_t* out_idx, float* out_score,
+                                 hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * idx_score_topk_witness

@@ -19,7 +19,8 @@ SI_OK = 0
 SI_F32, SI_BF16, SI_FP8_E4M3FN = 0, 1, 2
 STATUS_NAMES = {0: "SI_OK", 1: "SI_ERR_INVALID_ARGUMENT", 2: "SI_ERR_ROWS_MISMATCH",
                 3: "SI_ERR_SEGMENTS_OUT_OF_RANGE", 4: "SI_ERR_LEARNED_KEEP_OUT_OF_RANGE",
-                5: "SI_ERR_UNSUPPORTED_DTYPE", 6: "SI_ERR_WORKSPACE_TOO_SMALL", 7: "SI_ERR_DEVICE"}
+                5: "SI_ERR_UNSUPPORTED_DTYPE", 6: "SI_ERR_WORKSPACE_TOO_SMALL", 7: "SI_ERR_DEVICE",
+                8: "SI_ERR_SCRATCH_LIMIT"}
 
 
 class SparseIndexerError(RuntimeError):
@@ -46,6 +47,8 @@ SIGNATURES = {
     "idx_score_topk": (i32, [vp, i32, vp, i32, vp, vp, i64, vp, vp, i32, i32, i32, i64, i64, i32,
                              vp, vp, vp, sz, vp]),
     "idx_score_topk_workspace": (sz, [i32, i32, i32, i64, i32]),
+    "idx_score_topk_noalloc": (i32, [vp, i32, vp, i32, vp, vp, i64, vp, vp, i32, i32, i32, i64,
+                                     i64, i32, vp, vp, vp]),
     "idx_score_topk_witness": (i32, [vp, i32, vp, i32, vp, vp, i64, vp, vp, i32, i32, i32, i64,
                                      i64, i32, vp, vp, vp, i32, i32, i32, vp, sz, vp]),
     "idx_score_topk_prior": (i32, [vp, i32, vp, i32, vp, vp, i64, vp, vp, i32, i32, i32, i64, i64,
@@ -174,6 +177,33 @@ def idx_score_topk(q, k, w, vis_len, topk, *, k_scale=None, k_row_offset=None, m
                               _ptr(vis_len), n_q, H, D, n_k, max_vis, topk, _ptr(out_idx),
                               _ptr(out_score), _ptr(ws), ws_bytes, _stream(dev))
     _check(st, "idx_score_topk")
+    return out_idx, out_score
+
+
+def idx_score_topk_noalloc(q, k, w, vis_len, topk, *, k_scale=None, k_row_offset=None,
+                           max_vis=None, out_idx=None, out_score=None, want_scores=True):
+    """idx_score_topk with the library's fixed scratch instead of a workspace
+    (the C call allocates nothing; this wrapper allocates the outputs only if
+    they are not given).  Returns (idx, scores|None)."""
+    _dev_tensor(q, "q")
+    _dev_tensor(k, "k")
+    _dev_tensor(w, "w", torch.float32)
+    _dev_tensor(vis_len, "vis_len", torch.int32)
+    dev = q.device
+    n_q, H, D = q.shape
+    n_k = k.shape[0]
+    if max_vis is None:
+        max_vis = _default_max_vis(n_k, k_row_offset, vis_len, n_q)
+    w_stride = H if w.dim() == 2 else 0
+    if out_idx is None:
+        out_idx = torch.empty((n_q, topk), dtype=torch.int32, device=dev)
+    if out_score is None and want_scores:
+        out_score = torch.empty((n_q, topk), dtype=torch.float32, device=dev)
+    st = lib().idx_score_topk_noalloc(_ptr(q), _dtype_code(q, "q"), _ptr(k), _dtype_code(k, "k"),
+                                      _ptr(k_scale), _ptr(w), w_stride, _ptr(k_row_offset),
+                                      _ptr(vis_len), n_q, H, D, n_k, max_vis, topk,
+                                      _ptr(out_idx), _ptr(out_score), _stream(dev))
+    _check(st, "idx_score_topk_noalloc")
     return out_idx, out_score
 
 

@@ -2,7 +2,16 @@
 // carving and launches on the caller's stream.  See include/sparse_indexer.h.
 #include <string.h>
 
+#include <mutex>
+
 #include "si_internal.hpp"
+
+// The allocation-free entry point's scratch: the score rows and candidate
+// lists that idx_score_topk keeps in the caller's workspace.  One copy per
+// GPU, held from the library's load on that GPU until the process ends.
+// Host code never uses this name as an address: it takes the device
+// address from hipGetSymbolAddress (scratch_on_device below).
+static __device__ __align__(256) unsigned char scratch[SI_NOALLOC_SCRATCH_BYTES];
 
 namespace si {
 hipError_t launch_block_select(const float* q, const float* k, const int64_t* qpos, int32_t n_q,
@@ -39,6 +48,8 @@ const char* si_status_string(si_status s) {
     case SI_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
     case SI_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case SI_ERR_DEVICE: return "device error";
+    case SI_ERR_SCRATCH_LIMIT:
+      return "problem needs more than the allocation-free entry point's fixed scratch";
   }
   return "unknown status";
 }
@@ -149,6 +160,60 @@ si_status idx_score_topk(const void* q, si_dtype q_dtype, const void* k, si_dtyp
   hipError_t e = launch_score(sa, stream);
   if (e == hipSuccess) e = launch_topk(ta, stream);
   return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
+}
+
+// Device address of `scratch` on the device of `stream` (the current device
+// for the null stream), looked up once per device with that device current
+// and kept; nullptr on failure.
+static void* scratch_on_device(hipStream_t stream) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t d;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return nullptr;
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+si_status idx_score_topk_noalloc(const void* q, si_dtype q_dtype, const void* k, si_dtype k_dtype,
+                                 const float* k_scale, const float* w, int64_t w_row_stride,
+                                 const int64_t* k_row_offset, const int32_t* vis_len,
+                                 int32_t n_q, int32_t H, int32_t D, int64_t n_k, int64_t max_vis,
+                                 int32_t topk, int32_t* out_idx, float* out_score,
+                                 hipStream_t stream) {
+  // every host-side check first (as idx_score_topk's), then the size limit;
+  // only then the one runtime query (no allocation: the array exists since
+  // the library's code object was loaded on the device)
+  ScoreArgs sa;
+  si_status s = check_score_args(q, q_dtype, k, k_dtype, k_scale, w, w_row_stride, k_row_offset,
+                                 vis_len, n_q, H, D, n_k, max_vis, &sa);
+  if (s != SI_OK) return s;
+  if (topk < 1 || topk > kMaxTopk) return SI_ERR_INVALID_ARGUMENT;
+  if (n_q == 0) return SI_OK;
+  if (!out_idx || !aligned4(out_idx) || (out_score && !aligned4(out_score)))
+    return SI_ERR_INVALID_ARGUMENT;
+  const size_t need = idx_score_topk_workspace(n_q, H, D, max_vis, topk);
+  if (need > SI_NOALLOC_SCRATCH_BYTES) return SI_ERR_SCRATCH_LIMIT;
+  void* ws = scratch_on_device(stream);
+  if (ws == nullptr) return SI_ERR_DEVICE;
+  return idx_score_topk(q, q_dtype, k, k_dtype, k_scale, w, w_row_stride, k_row_offset, vis_len,
+                        n_q, H, D, n_k, max_vis, topk, out_idx, out_score, ws,
+                        SI_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 si_status idx_score_topk_witness(const void* q, si_dtype q_dtype, const void* k, si_dtype k_dtype,

@@ -12,7 +12,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, INVALID, ROWS_MISMATCH, SEGS, KEEP, DTYPE, WS, DEVICE = range(8)
+OK, INVALID, ROWS_MISMATCH, SEGS, KEEP, DTYPE, WS, DEVICE, SCRATCH = range(9)
 
 
 def _declared_functions():
@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(8):
+    for s in range(9):
         assert L.si_status_string(s)
     assert b"64" in L.si_status_string(SEGS)
 
@@ -116,6 +116,48 @@ def test_idx_score_topk_refusals(L):
     assert call(n_q=0) == OK
     np.testing.assert_array_equal(out, 7)
     np.testing.assert_array_equal(outs, 7.0)
+
+
+def test_idx_score_topk_noalloc_refusals(L):
+    """The allocation-free entry point makes idx_score_topk's host checks,
+    then refuses problems beyond its fixed scratch, all before any HIP call."""
+    n_q, H, D, n_k, K = 4, 64, 128, 100, 16
+    q = np.zeros(n_q * H * D + 8, np.uint16)
+    k = np.zeros(n_k * D + 8, np.uint16)
+    w = np.zeros(n_q * H, np.float32)
+    vis = np.full(n_q, n_k, np.int32)
+    out = np.full(n_q * K, 7, np.int32)
+    outs = np.full(n_q * K, 7.0, np.float32)
+
+    def al(a):
+        return a.ctypes.data + (-a.ctypes.data) % 16
+
+    base = dict(q=al(q), qd=1, k=al(k), kd=1, ks=None, w=_p(w), ws_=H, off=None, vis=_p(vis),
+                n_q=n_q, H=H, D=D, n_k=n_k, mv=n_k, K=K, oi=_p(out), os=_p(outs))
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.idx_score_topk_noalloc(a["q"], a["qd"], a["k"], a["kd"], a["ks"], a["w"],
+                                        a["ws_"], a["off"], a["vis"], a["n_q"], a["H"], a["D"],
+                                        a["n_k"], a["mv"], a["K"], a["oi"], a["os"], None)
+
+    assert call(K=0) == INVALID
+    assert call(K=4097) == INVALID
+    assert call(n_q=-1) == INVALID
+    assert call(qd=2) == DTYPE
+    assert call(q=None) == INVALID
+    assert call(oi=None) == INVALID
+    assert call(q=al(q) + 2) == INVALID
+    assert call(n_q=0) == OK
+    # 128 MiB of scratch: 4096 rows x 8192 keys fit exactly, one more row does not
+    limit = 128 << 20
+    assert L.idx_score_topk_workspace(4096, H, D, 8192, K) == limit
+    assert L.idx_score_topk_workspace(4097, H, D, 8192, K) > limit
+    assert call(n_q=4097, mv=8192, n_k=8192) == SCRATCH
+    assert call(n_q=8192, mv=8192, n_k=8192, K=2048) == SCRATCH
+    np.testing.assert_array_equal(out, 7)
+    np.testing.assert_array_equal(outs, 7.0)
+    assert b"scratch" in L.si_status_string(SCRATCH)
 
 
 def test_idx_score_topk_witness_refusals(L):
