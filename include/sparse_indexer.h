@@ -5,6 +5,7 @@
  * Operations, each defined by the page cited at its declaration:
  *   idx_score_topk       lightning-indexer score + per-query top-K
  *   idx_score_topk_witness idx_score_topk then kvwitness_merge, in one pass
+ *   idx_score_topk_fused the same from a single kernel (prefill layout)
  *   idx_score_topk_prior the same result on the decode path, selecting only
  *                        among keys above a threshold from recent keys
  *   dosa_prune_topk      the same top-K through DoSA's certified prune
@@ -166,6 +167,32 @@ si_status idx_score_topk_witness(const void* q, si_dtype q_dtype, const void* k,
                                  const int32_t* context_lens, int32_t num_segments, int32_t keep,
                                  int32_t max_replacements, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * idx_score_topk_fused
+ *
+ * idx_score_topk_witness computed by ONE kernel for the prefill layout: each
+ * workgroup scores its query rows, writes them to the workspace and selects
+ * their top-K (then the witness merge) while the rows are still in cache -
+ * the score writeback and selection input the DoSA reading notes, section 5,
+ * name as costs.  Results equal idx_score_topk_witness's bit for bit (and
+ * idx_score_topk's when num_segments or the budget is 0).  On MI355X it is
+ * slower than idx_score_topk_witness's two kernels at every prefill size
+ * measured (8192 x 8192 H64: 0.55 against 0.51 ms), because a workgroup's
+ * selection stalls the MFMA work that would otherwise run on its SIMDs; it
+ * is kept for callers that want one launch.
+ * Supported: k_row_offset NULL (shared keys), bf16 q and k, H <= 64, D 64 or
+ * 128, n_k * D * 2 <= 2 MiB, max_vis <= 8192, topk <= 2048; other shapes ->
+ * SI_ERR_UNSUPPORTED_DTYPE.  Arguments, workspace and other errors as
+ * idx_score_topk_witness.
+ * ------------------------------------------------------------------------ */
+si_status idx_score_topk_fused(const void* q, si_dtype q_dtype, const void* k, si_dtype k_dtype,
+                               const float* k_scale, const float* w, int64_t w_row_stride,
+                               const int64_t* k_row_offset, const int32_t* vis_len, int32_t n_q,
+                               int32_t H, int32_t D, int64_t n_k, int64_t max_vis, int32_t topk,
+                               int32_t* out_idx, float* out_score, const int32_t* context_lens,
+                               int32_t num_segments, int32_t keep, int32_t max_replacements,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * idx_score_topk_prior

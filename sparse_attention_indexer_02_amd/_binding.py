@@ -51,6 +51,8 @@ SIGNATURES = {
                                      i64, i32, vp, vp, vp]),
     "idx_score_topk_witness": (i32, [vp, i32, vp, i32, vp, vp, i64, vp, vp, i32, i32, i32, i64,
                                      i64, i32, vp, vp, vp, i32, i32, i32, vp, sz, vp]),
+    "idx_score_topk_fused": (i32, [vp, i32, vp, i32, vp, vp, i64, vp, vp, i32, i32, i32, i64,
+                                   i64, i32, vp, vp, vp, i32, i32, i32, vp, sz, vp]),
     "idx_score_topk_prior": (i32, [vp, i32, vp, i32, vp, vp, i64, vp, vp, i32, i32, i32, i64, i64,
                                    i32, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
     "idx_score_topk_prior_workspace": (sz, [i32, i64, i32]),
@@ -209,9 +211,11 @@ def idx_score_topk_noalloc(q, k, w, vis_len, topk, *, k_scale=None, k_row_offset
 
 def idx_score_topk_witness(q, k, w, vis_len, topk, context_lens, num_segments, *, keep=None,
                            max_replacements=None, k_scale=None, k_row_offset=None, max_vis=None,
-                           out_idx=None, out_score=None, want_scores=True, workspace=None):
+                           out_idx=None, out_score=None, want_scores=True, workspace=None,
+                           fused=False):
     """idx_score_topk then the segment-witness merge of its rows, in one pass;
     keep/max_replacements default to the serving convention (topk - S, S).
+    fused=True calls idx_score_topk_fused (one kernel; prefill layout only).
     Returns (idx, scores|None)."""
     _dev_tensor(q, "q")
     _dev_tensor(k, "k")
@@ -234,13 +238,13 @@ def idx_score_topk_witness(q, k, w, vis_len, topk, context_lens, num_segments, *
         out_score = torch.empty((n_q, topk), dtype=torch.float32, device=dev)
     need = lib().idx_score_topk_workspace(n_q, H, D, max_vis, topk)
     ws, ws_bytes = _workspace(need, dev, workspace)
-    st = lib().idx_score_topk_witness(_ptr(q), _dtype_code(q, "q"), _ptr(k), _dtype_code(k, "k"),
-                                      _ptr(k_scale), _ptr(w), w_stride, _ptr(k_row_offset),
-                                      _ptr(vis_len), n_q, H, D, n_k, max_vis, topk,
-                                      _ptr(out_idx), _ptr(out_score), _ptr(context_lens),
-                                      num_segments, keep, max_replacements, _ptr(ws), ws_bytes,
-                                      _stream(dev))
-    _check(st, "idx_score_topk_witness")
+    name = "idx_score_topk_fused" if fused else "idx_score_topk_witness"
+    st = getattr(lib(), name)(_ptr(q), _dtype_code(q, "q"), _ptr(k), _dtype_code(k, "k"),
+                              _ptr(k_scale), _ptr(w), w_stride, _ptr(k_row_offset),
+                              _ptr(vis_len), n_q, H, D, n_k, max_vis, topk, _ptr(out_idx),
+                              _ptr(out_score), _ptr(context_lens), num_segments, keep,
+                              max_replacements, _ptr(ws), ws_bytes, _stream(dev))
+    _check(st, name)
     return out_idx, out_score
 
 

@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsparse_indexer.so")
 SOURCES = ["api.hip", "score.hip", "topk.hip", "witness.hip", "block_select.hip", "dosa.hip",
-           "prior.hip", "consume.hip"]
+           "prior.hip", "consume.hip", "prefill_fused.hip"]
 ARCH = os.environ.get("SI_OFFLOAD_ARCH", "gfx950")
 
 COMMON = ["hipcc", f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

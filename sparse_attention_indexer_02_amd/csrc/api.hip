@@ -130,6 +130,50 @@ si_status rows_topk(const float* scores, int64_t score_stride, const int32_t* vi
   return launch_topk(ta, stream) == hipSuccess ? SI_OK : SI_ERR_DEVICE;
 }
 
+// Validates an idx_score_topk call and fills the score and top-K stage
+// arguments (the workspace holds the score rows, then the candidate lists);
+// *done is set when there is nothing to launch (n_q == 0).
+static si_status prepare_score_topk(const void* q, si_dtype q_dtype, const void* k,
+                                    si_dtype k_dtype, const float* k_scale, const float* w,
+                                    int64_t w_row_stride, const int64_t* k_row_offset,
+                                    const int32_t* vis_len, int32_t n_q, int32_t H, int32_t D,
+                                    int64_t n_k, int64_t max_vis, int32_t topk, int32_t* out_idx,
+                                    float* out_score, void* workspace, size_t workspace_bytes,
+                                    ScoreArgs* sa, TopkArgs* ta, bool* done) {
+  *done = false;
+  si_status s = check_score_args(q, q_dtype, k, k_dtype, k_scale, w, w_row_stride, k_row_offset,
+                                 vis_len, n_q, H, D, n_k, max_vis, sa);
+  if (s != SI_OK) return s;
+  if (topk < 1 || topk > kMaxTopk) return SI_ERR_INVALID_ARGUMENT;
+  if (n_q == 0) {
+    *done = true;
+    return SI_OK;
+  }
+  if (!out_idx || !aligned4(out_idx) || (out_score && !aligned4(out_score)))
+    return SI_ERR_INVALID_ARGUMENT;
+  const size_t need = idx_score_topk_workspace(n_q, H, D, max_vis, topk);
+  if (need && (!workspace || workspace_bytes < need ||
+               (reinterpret_cast<uintptr_t>(workspace) & 255)))
+    return SI_ERR_WORKSPACE_TOO_SMALL;
+  sa->scores = reinterpret_cast<float*>(workspace);
+  const size_t cand_off = (score_ws_bytes(n_q, max_vis) + 255) & ~(size_t)255;
+  TopkArgs& t = *ta;
+  t.scores = sa->scores; t.stride = max_vis; t.vis_len = vis_len; t.k_row_offset = k_row_offset;
+  t.n_k = n_k; t.max_vis = max_vis; t.n_rows = n_q; t.K = topk; t.out_idx = out_idx;
+  t.out_score = out_score; t.id_map = nullptr;
+  t.workspace = static_cast<unsigned char*>(workspace) + cand_off;
+  t.workspace_bytes = workspace_bytes - cand_off;
+  return SI_OK;
+}
+
+// The score kernel, then the top-K kernel (which also merges witnesses when
+// ta.wit_lens is set).
+static si_status run_score_topk(const ScoreArgs& sa, const TopkArgs& ta, hipStream_t stream) {
+  hipError_t e = launch_score(sa, stream);
+  if (e == hipSuccess) e = launch_topk(ta, stream);
+  return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
+}
+
 si_status idx_score_topk(const void* q, si_dtype q_dtype, const void* k, si_dtype k_dtype,
                          const float* k_scale, const float* w, int64_t w_row_stride,
                          const int64_t* k_row_offset, const int32_t* vis_len, int32_t n_q,
@@ -137,29 +181,32 @@ si_status idx_score_topk(const void* q, si_dtype q_dtype, const void* k, si_dtyp
                          int32_t* out_idx, float* out_score, void* workspace,
                          size_t workspace_bytes, hipStream_t stream) {
   ScoreArgs sa;
-  si_status s = check_score_args(q, q_dtype, k, k_dtype, k_scale, w, w_row_stride, k_row_offset,
-                                 vis_len, n_q, H, D, n_k, max_vis, &sa);
-  if (s != SI_OK) return s;
-  if (topk < 1 || topk > kMaxTopk) return SI_ERR_INVALID_ARGUMENT;
-  if (n_q == 0) return SI_OK;
-  if (!out_idx || !aligned4(out_idx) || (out_score && !aligned4(out_score)))
-    return SI_ERR_INVALID_ARGUMENT;
-  const size_t need = idx_score_topk_workspace(n_q, H, D, max_vis, topk);
-  if (need && (!workspace || workspace_bytes < need ||
-               (reinterpret_cast<uintptr_t>(workspace) & 255)))
-    return SI_ERR_WORKSPACE_TOO_SMALL;
-  sa.scores = reinterpret_cast<float*>(workspace);
-  const size_t cand_off = (score_ws_bytes(n_q, max_vis) + 255) & ~(size_t)255;
-
   TopkArgs ta;
-  ta.scores = sa.scores; ta.stride = max_vis; ta.vis_len = vis_len; ta.k_row_offset = k_row_offset;
-  ta.n_k = n_k; ta.max_vis = max_vis; ta.n_rows = n_q; ta.K = topk; ta.out_idx = out_idx;
-  ta.out_score = out_score; ta.id_map = nullptr;
-  ta.workspace = static_cast<unsigned char*>(workspace) + cand_off;
-  ta.workspace_bytes = workspace_bytes - cand_off;
-  hipError_t e = launch_score(sa, stream);
-  if (e == hipSuccess) e = launch_topk(ta, stream);
-  return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
+  bool done;
+  const si_status s = prepare_score_topk(q, q_dtype, k, k_dtype, k_scale, w, w_row_stride,
+                                         k_row_offset, vis_len, n_q, H, D, n_k, max_vis, topk,
+                                         out_idx, out_score, workspace, workspace_bytes, &sa, &ta,
+                                         &done);
+  if (s != SI_OK || done) return s;
+  return run_score_topk(sa, ta, stream);
+}
+
+// The witness merge's refusals, in kvwitness_merge's order (a refused call
+// writes nothing); *B gets the merge budget min(max_replacements, topk -
+// keep).
+static si_status check_witness_args(int32_t n_q, int32_t topk, const int32_t* out_idx,
+                                    const int32_t* context_lens, int32_t num_segments,
+                                    int32_t keep, int32_t max_replacements, int32_t* B) {
+  if (n_q < 0 || topk < 0 || keep < 0 || max_replacements < 0) return SI_ERR_INVALID_ARGUMENT;
+  if (n_q > 0 && !context_lens) return SI_ERR_ROWS_MISMATCH;
+  if (n_q > 0 && topk > 0 && !out_idx) return SI_ERR_INVALID_ARGUMENT;
+  if (num_segments < 0 || num_segments > SI_MAX_TOPOLOGY_SEGMENTS)
+    return SI_ERR_SEGMENTS_OUT_OF_RANGE;
+  if (keep > topk) return SI_ERR_LEARNED_KEEP_OUT_OF_RANGE;
+  *B = max_replacements < topk - keep ? max_replacements : topk - keep;
+  if (n_q > 0 && num_segments > 0 && *B > 0 && !aligned4(context_lens))
+    return SI_ERR_INVALID_ARGUMENT;
+  return SI_OK;
 }
 
 // Device address of `scratch` on the device of `stream` (the current device
@@ -224,44 +271,48 @@ si_status idx_score_topk_witness(const void* q, si_dtype q_dtype, const void* k,
                                  const int32_t* context_lens, int32_t num_segments, int32_t keep,
                                  int32_t max_replacements, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
-  // the merge's refusals first, in kvwitness_merge's order, then the
-  // indexer's; a refused call writes nothing
-  if (n_q < 0 || topk < 0 || keep < 0 || max_replacements < 0) return SI_ERR_INVALID_ARGUMENT;
-  if (n_q > 0 && !context_lens) return SI_ERR_ROWS_MISMATCH;
-  if (n_q > 0 && topk > 0 && !out_idx) return SI_ERR_INVALID_ARGUMENT;
-  if (num_segments < 0 || num_segments > SI_MAX_TOPOLOGY_SEGMENTS)
-    return SI_ERR_SEGMENTS_OUT_OF_RANGE;
-  if (keep > topk) return SI_ERR_LEARNED_KEEP_OUT_OF_RANGE;
-  const int32_t B = max_replacements < topk - keep ? max_replacements : topk - keep;
-  if (num_segments == 0 || B == 0)
-    return idx_score_topk(q, q_dtype, k, k_dtype, k_scale, w, w_row_stride, k_row_offset,
-                          vis_len, n_q, H, D, n_k, max_vis, topk, out_idx, out_score, workspace,
-                          workspace_bytes, stream);
-  if (n_q > 0 && !aligned4(context_lens)) return SI_ERR_INVALID_ARGUMENT;
-  ScoreArgs sa;
-  si_status s = check_score_args(q, q_dtype, k, k_dtype, k_scale, w, w_row_stride, k_row_offset,
-                                 vis_len, n_q, H, D, n_k, max_vis, &sa);
+  // the merge's refusals first, then the indexer's
+  int32_t B;
+  si_status s = check_witness_args(n_q, topk, out_idx, context_lens, num_segments, keep,
+                                   max_replacements, &B);
   if (s != SI_OK) return s;
-  if (topk < 1 || topk > kMaxTopk) return SI_ERR_INVALID_ARGUMENT;
-  if (n_q == 0) return SI_OK;
-  if (!out_idx || !aligned4(out_idx) || (out_score && !aligned4(out_score)))
-    return SI_ERR_INVALID_ARGUMENT;
-  const size_t need = idx_score_topk_workspace(n_q, H, D, max_vis, topk);
-  if (need && (!workspace || workspace_bytes < need ||
-               (reinterpret_cast<uintptr_t>(workspace) & 255)))
-    return SI_ERR_WORKSPACE_TOO_SMALL;
-  sa.scores = reinterpret_cast<float*>(workspace);
-  const size_t cand_off = (score_ws_bytes(n_q, max_vis) + 255) & ~(size_t)255;
+  ScoreArgs sa;
   TopkArgs ta;
-  ta.scores = sa.scores; ta.stride = max_vis; ta.vis_len = vis_len; ta.k_row_offset = k_row_offset;
-  ta.n_k = n_k; ta.max_vis = max_vis; ta.n_rows = n_q; ta.K = topk; ta.out_idx = out_idx;
-  ta.out_score = out_score; ta.id_map = nullptr;
-  ta.workspace = static_cast<unsigned char*>(workspace) + cand_off;
-  ta.workspace_bytes = workspace_bytes - cand_off;
-  ta.wit_lens = context_lens; ta.wit_S = num_segments; ta.wit_keep = keep; ta.wit_B = B;
-  hipError_t e = launch_score(sa, stream);
-  if (e == hipSuccess) e = launch_topk(ta, stream);
-  return e == hipSuccess ? SI_OK : SI_ERR_DEVICE;
+  bool done;
+  s = prepare_score_topk(q, q_dtype, k, k_dtype, k_scale, w, w_row_stride, k_row_offset, vis_len,
+                         n_q, H, D, n_k, max_vis, topk, out_idx, out_score, workspace,
+                         workspace_bytes, &sa, &ta, &done);
+  if (s != SI_OK || done) return s;
+  if (num_segments > 0 && B > 0) {
+    ta.wit_lens = context_lens; ta.wit_S = num_segments; ta.wit_keep = keep; ta.wit_B = B;
+  }
+  return run_score_topk(sa, ta, stream);
+}
+
+si_status idx_score_topk_fused(const void* q, si_dtype q_dtype, const void* k, si_dtype k_dtype,
+                               const float* k_scale, const float* w, int64_t w_row_stride,
+                               const int64_t* k_row_offset, const int32_t* vis_len, int32_t n_q,
+                               int32_t H, int32_t D, int64_t n_k, int64_t max_vis, int32_t topk,
+                               int32_t* out_idx, float* out_score, const int32_t* context_lens,
+                               int32_t num_segments, int32_t keep, int32_t max_replacements,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int32_t B;
+  si_status s = check_witness_args(n_q, topk, out_idx, context_lens, num_segments, keep,
+                                   max_replacements, &B);
+  if (s != SI_OK) return s;
+  ScoreArgs sa;
+  TopkArgs ta;
+  bool done;
+  s = prepare_score_topk(q, q_dtype, k, k_dtype, k_scale, w, w_row_stride, k_row_offset, vis_len,
+                         n_q, H, D, n_k, max_vis, topk, out_idx, out_score, workspace,
+                         workspace_bytes, &sa, &ta, &done);
+  if (s != SI_OK) return s;
+  if (!score_topk_fused_supported(sa, topk)) return SI_ERR_UNSUPPORTED_DTYPE;
+  if (done) return SI_OK;
+  if (num_segments > 0 && B > 0) {
+    ta.wit_lens = context_lens; ta.wit_S = num_segments; ta.wit_keep = keep; ta.wit_B = B;
+  }
+  return launch_score_topk_fused(sa, ta, stream) == hipSuccess ? SI_OK : SI_ERR_DEVICE;
 }
 
 size_t idx_score_topk_prior_workspace(int32_t n_q, int64_t max_vis, int32_t topk) {

@@ -40,7 +40,7 @@ __device__ __forceinline__ void score_group_shared(
   constexpr int CPT = (CHUNKS + 255) / 256;    // chunks per thread
   unsigned char (*lds)[32 * ROWB] = reinterpret_cast<unsigned char (*)[32 * ROWB]>(lds_base);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_index();
   auto row_of = [&](int i) -> int {  // slot i of this workgroup -> row, or -1
     int s = g * QB + i;
     if (s >= n_act) return -1;
@@ -119,6 +119,9 @@ __device__ __forceinline__ void score_group_shared(
     float sc[QPW];
 #pragma unroll
     for (int i = 0; i < QPW; ++i) sc[i] = head_reduce<MT>(acc[i], wv[i]);
+    // the stash waits for the prefetch: keep it after the head sums, so the
+    // load has the whole tile's MFMAs and epilogue to land
+    __builtin_amdgcn_sched_barrier(0);
     // buffer (t + 1) & 1 held tile t - 1, read before the previous barrier
     stash((t + 1) & 1);
     // lanes 32-63 hold the same sums; their out-of-range offset drops them

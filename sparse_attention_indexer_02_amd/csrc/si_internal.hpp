@@ -11,6 +11,13 @@ namespace si {
 
 constexpr int kWave = 64;
 
+// This thread's wave within the workgroup, as a value the compiler knows to
+// be uniform across the wave (so that what is derived from it - row
+// indices, buffer resources - stays in scalar registers).
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // ---------------------------------------------------------------------------
 // Orderable 32-bit keys: larger key <=> larger float.  -0 is folded onto +0
 // so that IEEE-equal scores tie and fall through to the index.
@@ -239,6 +246,11 @@ constexpr int kBlockTopkMaxN = 8192;
 constexpr int kBlockTopkMaxK = 2048;
 size_t topk_workspace_bytes(int64_t n_rows, int64_t max_vis, int K);
 constexpr int kMaxTopk = 4096;
+// Score and top-K of the prefill layout in one kernel: the shapes it takes
+// (shared bf16 keys in one key segment, rows of at most 8192 keys, K <=
+// 2048), and the launch (ta.scores must be a.scores with stride max_vis).
+bool score_topk_fused_supported(const ScoreArgs& a, int K);
+hipError_t launch_score_topk_fused(const ScoreArgs& a, const TopkArgs& ta, hipStream_t st);
 hipError_t launch_score_rows_listed(const ScoreArgs& a, const int32_t* row_list,
                                     const int32_t* row_count, hipStream_t st);
 

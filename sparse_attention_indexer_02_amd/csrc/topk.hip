@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkArgs a) {
 template <bool WIT, bool CHUNK>
 __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(8))) void topk_block(
     TopkArgs a) {
-  __shared__ TopkSmem S;
+  __shared__ TopkSmem<kBT> S;
   int r = (int)blockIdx.x;
   if (a.row_list) {
     if (r >= *a.row_count) return;
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(8))) void t
   } else {
     r = a.n_rows - 1 - r;  // causal rows grow with the index: longest first
   }
-  topk_row_block<WIT, CHUNK>(a, r, (int)blockIdx.y, S);
+  topk_row_block<kBT, kBN / kBT, WIT, CHUNK>(a, r, (int)blockIdx.y, S);
 }
 
 // Bytes of one chunk level (candidate ids + scores + per-row counts), and

@@ -1,6 +1,6 @@
-// Per-row top-K with one 512-thread workgroup and the row in registers,
-// for rows of at most 8192 scores and K <= 2048 (the block kernel of the
-// top-K stage and its chunk passes).
+// Per-row top-K with one workgroup and the row in registers, for rows of at
+// most 8192 scores and K <= 2048 (the block kernel of the top-K stage and its
+// chunk passes, and the top-K phase of the fused prefill kernel).
 #pragma once
 
 #include "witness_seg.hpp"
@@ -8,14 +8,15 @@
 namespace si {
 
 // ---------------------------------------------------------------------------
-// Rows of at most 8192 scores, K <= 2048: one 512-thread workgroup per row,
-// 16 scores per thread (eight waves per row: with four rows per CU, limited
-// by LDS, the CU holds its full 32 waves, and more waves per row measured
-// faster than more registers per thread).  Thread t holds the float4 groups
-// t, t + 512, t + 1024, t + 1536 of the row (positions 4 t + 2048 j + c),
-// so the workgroup's four loads of group row j read 8 KB contiguous, and a
-// row of n scores keeps all eight waves busy on its first ceil(n / 2048)
-// group rows (the rest are skipped uniformly).
+// Rows of at most 8192 scores, K <= 2048: one workgroup of T threads per
+// row, P = 8192 / T scores per thread (the top-K kernel: T = 512, P = 16,
+// eight waves per row: with four rows per CU, limited by LDS, the CU holds
+// its full 32 waves, and more waves per row measured faster than more
+// registers per thread; the fused prefill kernel: T = 256, P = 32).  Thread
+// t holds the float4 groups t, t + T, t + 2T, ... of the row (positions
+// 4 t + 4 T j + c), so the workgroup's loads of group row j read 16 T bytes
+// contiguous, and a row of n scores keeps every wave busy on its first
+// ceil(n / 4T) group rows (the rest are skipped uniformly).
 //  A. load (a NaN score is taken as -inf) and the row's value range;
 //  B. histogram over 4096 bins linear in score value over [vmin, vmax];
 //  C. scan from the top bin: the bin b1 holding the K-th item, and per bin
@@ -42,15 +43,10 @@ namespace si {
 // (8191 - position); composites compare as (score desc, index asc), and the
 // bin rides along so the rank step need not recompute it.
 // ---------------------------------------------------------------------------
-constexpr int kBT = 512;              // threads per row
-constexpr int kBPer = 16;             // positions per thread
-constexpr int kBN = kBT * kBPer;      // 8192
-static_assert(kBN == kBlockTopkMaxN, "block top-K row capacity");
-constexpr int kBGroups = kBPer / 4;   // float4 groups per thread
-constexpr int kBStep = 4 * kBT;       // positions per group row
+constexpr int kBT = 512;              // threads per row of the top-K kernel
+constexpr int kBN = kBlockTopkMaxN;   // row capacity (8192): threads x positions per thread
 constexpr int kBK = kBlockTopkMaxK;   // largest K (2048)
 constexpr int kBins = 4096;           // value bins
-constexpr int kBinsPer = kBins / kBT;
 constexpr int kBrute = 256;           // largest b1 ranked item by item
 constexpr int kCrowd = 64;            // largest per-bin count ranked by scanning the bin
 constexpr int kPosBits = 13;          // positions < kBN
@@ -76,7 +72,7 @@ struct alignas(16) BlockSmem {
 // Owner search over nb bins from the top (thread t owns nb/kBT consecutive
 // bins, highest first): the bin holding the want-th item from the top, the
 // items above it and its count.  get(b) reads bin b's count.
-template <class Get>
+template <int kBT, class Get>
 __device__ __forceinline__ void find_from_top(Get get, int nb, int want, int* red, int* bin,
                                               int* above, int* count) {
   const int t = threadIdx.x;
@@ -106,6 +102,7 @@ __device__ __forceinline__ void find_from_top(Get get, int nb, int want, int* re
   __syncthreads();
 }
 
+template <int kBT>
 struct TopkSmem {
   BlockSmem sm;
   int red[kBT / 64 + 8];
@@ -121,8 +118,15 @@ struct TopkSmem {
 // plain build's register budget, so the plain build leaves it out).
 // CHUNK: the build for chunk passes (a.chunk > 0), which end after the
 // selection; the final pass (a.chunk == 0) takes CHUNK false.
-template <bool WIT, bool CHUNK>
-__device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy, TopkSmem& S) {
+template <int kBT, int kBPer, bool WIT, bool CHUNK>
+__device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
+                                               TopkSmem<kBT>& S) {
+  static_assert(kBT * kBPer == kBN, "threads x positions per thread = row capacity");
+  static_assert(kBPer % 4 == 0 && kBPer <= 32, "float4 groups; one mask bit per position");
+  static_assert(kBT >= kBN / 32 && kBT % 64 == 0, "one thread per word of the tie bitmap");
+  constexpr int kBGroups = kBPer / 4;   // float4 groups per thread
+  constexpr int kBStep = 4 * kBT;       // positions per group row
+  constexpr int kBinsPer = kBins / kBT;
   BlockSmem& sm = S.sm;
   int* red = S.red;
   float (*fred)[kBT / 64] = S.fred;
@@ -277,7 +281,7 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   //    this thread's float4: one block scan of the four per-group counts,
   //    packed 16 bits each (a group row holds at most 2048).
   auto chunk_out = [&](const uint32_t selm) {
-    static_assert(kBGroups == 4, "four group rows, two packed counts per scan word");
+    static_assert(!CHUNK || kBGroups == 4, "four group rows, two packed counts per scan word");
     auto gcount = [&](int j) { return __builtin_popcount((selm >> (4 * j)) & 0xFu); };
     int tot01, tot23;
     const int p01 = block_excl_scan<kBT>(gcount(0) | (gcount(1) << 16), red, &tot01);
@@ -456,7 +460,8 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
         }
         __syncthreads();
         int dig, ab;
-        find_from_top([&](int b) { return sm.x.sub[b]; }, 2048, rank, red, &dig, &ab, &count);
+        find_from_top<kBT>([&](int b) { return sm.x.sub[b]; }, 2048, rank, red, &dig, &ab,
+                           &count);
         rank -= ab;
         above += ab;
         prefix |= (uint32_t)dig << sh;

@@ -135,3 +135,45 @@ def test_fused_budgets(S, keep, B):
     d = dev_inputs(cfg)
     say(f"fused witness budgets S={S} keep={keep} B={B}")
     _both(d, cfg, _lens(d), S, keep, B)
+
+
+def _one_kernel_equal(cfg, S, keep, B, label):
+    """idx_score_topk_fused (one kernel) against idx_score_topk_witness (score
+    kernel, then top-K kernel): ids and scores bit for bit."""
+    import sparse_attention_indexer_02_amd as si
+    d = dev_inputs(cfg)
+    K = cfg["topk"]
+    lens = _lens(d)
+    say(f"one-kernel prefill {label}: n_q={cfg['n_q']} L={cfg['n_k']} H={cfg['H']} "
+        f"D={cfg['D']} K={K} S={S}")
+    ri, rs = si.idx_score_topk_witness(d["q"], d["k"], d["w"], d["vis_len"], K, lens, S,
+                                       keep=keep, max_replacements=B)
+    fi, fs = si.idx_score_topk_witness(d["q"], d["k"], d["w"], d["vis_len"], K, lens, S,
+                                       keep=keep, max_replacements=B, fused=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(fi.cpu().numpy(), ri.cpu().numpy())
+    np.testing.assert_array_equal(fs.cpu().numpy().view(np.uint32), rs.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("n_q,L,H,D,K,S", [(96, 700, 64, 128, 128, 16), (61, 500, 32, 128, 64, 4),
+                                           (40, 2100, 64, 64, 300, 0), (9, 33, 20, 128, 48, 64)])
+def test_one_kernel_small(n_q, L, H, D, K, S):
+    cfg = synth.prefill(seed=n_q + L, n_q=n_q, L=L, H=H, D=D, topk=K, S=max(S, 1))
+    _one_kernel_equal(cfg, S, max(K - S, 0), S, "small")
+
+
+def test_one_kernel_full_prefill():
+    cfg = full_config("prefill")
+    w = cfg["witness"]
+    _one_kernel_equal(cfg, w["S"], w["keep"], w["max_rep"], "full size")
+
+
+def test_one_kernel_refuses_other_layouts():
+    import sparse_attention_indexer_02_amd as si
+    cfg = synth.decode(seed=8, rows=4, max_len=900, topk=64)
+    d = dev_inputs(cfg)
+    with pytest.raises(si.SparseIndexerError) as e:
+        si.idx_score_topk_witness(d["q"], d["k"], d["w"], d["vis_len"], 64, _lens(d), 8,
+                                  k_scale=d["k_scale"], k_row_offset=d["k_row_offset"],
+                                  max_vis=cfg["max_vis"], fused=True)
+    assert e.value.status == 5  # SI_ERR_UNSUPPORTED_DTYPE
