@@ -487,16 +487,27 @@ def bench_dosa(args):
                                                             ref_s.view(torch.int32)))
     surv = stats["n_survivors"].cpu().numpy().astype(np.int64)
     fb = stats["fallback"].cpu().numpy()
-    scanned = int((cfg["vis_len"].astype(np.int64) - dp["n_seeds"]).sum())
     kept = dp["kept_heads"]
-    head_dots = (n_q * dp["n_seeds"] * H + scanned * (kept + 1) +
-                 int(surv.clip(0).sum()) * H)
-    # MFMA work actually issued: seeds and survivors at H rows (32-row tiles),
-    # the bound at one 32-row tile per query
-    rows_tile = 32 * ((H + 31) // 32)
-    mfma_flops = 2.0 * D * (n_q * dp["n_seeds"] * rows_tile + pairs * 32 +
-                            int(surv.clip(0).sum()) * rows_tile)
-    ach = mfma_flops / per["dosa"] / 1e9
+    scanned_rows = cfg["vis_len"].astype(np.int64) - dp["n_seeds"]
+    # The method's own work (2 D flop per head-key dot): the representative
+    # rows over the common prefix, every row's seeds at H heads, and then per
+    # row either the bound over its other visible keys at kept + 1 rows plus
+    # its survivors at H heads, or (rows over the capacity) the exact path
+    # over every visible key at H heads.  The bound's rows beyond kept + 1
+    # (its 32-row MFMA tile) and a fallback row's partial bound are not
+    # counted.
+    vis64 = np.minimum(cfg["vis_len"].astype(np.int64), n_k)
+    c_common = int(vis64.min())
+    fbm = fb.astype(bool)
+    alg_dots = (dp["n_rep_queries"] * c_common * H + n_q * dp["n_seeds"] * H +
+                int(((vis64 - dp["n_seeds"])[~fbm]).sum()) * (kept + 1) +
+                int(surv.clip(0)[~fbm].sum()) * H + int(vis64[fbm].sum()) * H)
+    alg_flops = 2.0 * D * alg_dots
+    ach = alg_flops / per["dosa"] / 1e9
+    # survival over the rows that kept their pruned path (a row over the
+    # capacity stops counting once past it)
+    kept_scan = int(scanned_rows[~fbm].sum())
+    survival = float(surv[~fbm].sum()) / kept_scan if kept_scan > 0 else None
     out = dict(metric=METRIC, value=pairs / (wall_ms / 1e3), unit="pairs/s", n_gpus=1,
                steps=args.steps, warmup=args.warmup, ms_per_step=wall_ms, higher_is_better=True,
                scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
@@ -506,12 +517,13 @@ def bench_dosa(args):
                            pairs_per_step=pairs),
                roofline=dict(bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                              frac=ach / PEAK_BF16_TFLOPS, traffic=None,
-                             kernel="dosa_prune_topk (all kernels; MFMA flops issued)"),
+                             kernel="dosa_prune_topk (all kernels; the method's own head-key "
+                                    "dots, 2 D flop each)", algo_flops=alg_flops),
                dosa=dict(ms=per["dosa"], unpruned_ms=per_u["unpruned"],
                          speedup_vs_unpruned=per_u["unpruned"] / per["dosa"],
                          bit_identical_to_unpruned=equal,
-                         survival=float(surv.clip(0).sum()) / max(scanned, 1),
-                         fallback_rows=int(fb.sum()), head_dots=head_dots,
+                         survival_of_pruned_rows=survival,
+                         fallback_rows=int(fb.sum()), head_dots=alg_dots,
                          dense_head_dots=pairs * H,
                          shared_streams=dict(ms=per_g["groups"], survivors_shared=shared_n,
                                              bit_identical_to_unpruned=eq_g)))

@@ -279,9 +279,14 @@ size_t rows_topk_workspace(int32_t n_rows, int64_t max_vis, int32_t topk);
  *  params->n_rep_queries     representative rows for the cold prior (1..64),
  *                            row round(i (n_q-1)/(R-1)) for i = 0..R-1.
  *  params->rep_topk          top list length per representative row (1..4096).
- *  params->kept_heads        heads scored exactly in the bound (0..min(31, H)).
+ *  params->kept_heads        heads scored exactly in the bound (0..min(31, H)),
+ *                            the largest |w_h| * mean max(x_h, 0) over the
+ *                            activation sample: 128 seeds evenly spaced in
+ *                            seed order, round(i (n_seeds-1)/127) (all seeds
+ *                            when fewer; section 4 samples 128 positions of
+ *                            the seed region).
  *  params->neg_active_frac   omitted negative heads whose activation
- *                            frequency over the seeds is >= this are
+ *                            frequency over that sample is >= this are
  *                            aggregated; the rest are dropped (safe).
  *  params->seed_ids          device [n_seeds] strictly increasing key ids
  *                            visible to every row, or NULL for the cold
@@ -304,7 +309,9 @@ size_t rows_topk_workspace(int32_t n_rows, int64_t max_vis, int32_t topk);
  * [n_q, n_seeds], survivor lists [n_q, capacity] and, for the exact path,
  * full score rows [n_q, n_k] (f32).
  *  stats (optional, device pointers, each may be NULL): tau [n_q],
- *        n_survivors [n_q] (keys passing the bound), fallback [n_q] (1 when
+ *        n_survivors [n_q] (keys passing the bound; for a row over the
+ *        capacity, the count at which its scan stopped, above the
+ *        capacity), fallback [n_q] (1 when
  *        the row took the exact path), n_shared [n_q] (those of the row's
  *        survivors its group's shared stream carries; 0 without shared
  *        streams).

@@ -632,14 +632,15 @@ static void full_row_topk(const orc_problem* P, int32_t r, int32_t* out_idx, dou
  *     bounded through one kept anchor, q_h = beta q_j + d_h with beta >= 0:
  *     [q_h.k]_+ <= beta [q_j.k]_+ + |d_h| |k|, and
  *     (section 3.2) omitted negative heads active on at least neg_active_frac
- *     of the seeds aggregated as a_A = sum |w_h| q_h, deducting [a_A.k]_+,
+ *     of the sampled seeds aggregated as a_A = sum |w_h| q_h, deducting [a_A.k]_+,
  *     which never exceeds their true deduction.
  *     A key is excluded iff U < tau (U == tau is kept).
  *  3. survivors get their exact score; those below tau are dropped; the final
  *     top-K is taken over the seeds' top-K plus the kept survivors, by score.
- * Planning choices the pages leave open: activation statistics come from the
- * seeds; the kept heads are the kept_heads largest |w_h| * mean [x_h]_+ over
- * seeds (ties: lower head); an omitted positive head anchors on the kept
+ * Planning choices the pages leave open: activation statistics come from a
+ * 128-seed sample (section 4 samples 128 positions of the seed region); the
+ * kept heads are the kept_heads largest |w_h| * mean [x_h]_+ over the sample
+ * (ties: lower head); an omitted positive head anchors on the kept
  * head with the smallest residual under the clamped projection
  * beta = max(0, q_h.q_j / |q_j|^2) (ties: lower head).  The bound carries a
  * 1e-9 * sum_h |w_h| |q_h| |k| margin so double rounding can never make it
@@ -685,22 +686,31 @@ int32_t orc_dosa_row(const orc_problem* P, const orc_dosa_params* dp, const int3
   double* seed_top_s = (double*)malloc(sizeof(double) * K);
   load_query(P, r, qd, qn);
 
-  /* Step 1: the seed threshold. */
+  /* Step 1: the seed threshold.  The activation statistics come from a
+   * sample of the seeds ([DoSA] section 4: the planner counts activation
+   * patterns over 128 positions of the seed region): m = min(128, ns) seeds
+   * evenly spaced in seed order, seed index round(i (ns - 1) / (m - 1)). */
+  const int32_t m = ns < 128 ? ns : 128;
+  int32_t next_sample = 0, si = 0;  /* the next sample's seed index, and its i */
   for (int32_t i = 0; i < ns; ++i) {
     int64_t j = seeds[i];
     is_seed[j] = 1;
     double knorm = load_key(P, j, kd);
     seed_s[i] = score_key(qd, qn, w, H, D, kd, knorm, x, NULL, NULL);
-    for (int h = 0; h < H; ++h) {
-      if (x[h] > 0.0) {
-        act[h] += 1.0;
-        relu_mean[h] += x[h];
+    if (si < m && i == next_sample) {
+      for (int h = 0; h < H; ++h) {
+        if (x[h] > 0.0) {
+          act[h] += 1.0;
+          relu_mean[h] += x[h];
+        }
       }
+      ++si;
+      next_sample = m > 1 ? (int32_t)((2LL * si * (ns - 1) + (m - 1)) / (2LL * (m - 1))) : ns;
     }
   }
   for (int h = 0; h < H; ++h) {
-    act[h] /= ns;
-    relu_mean[h] /= ns;
+    act[h] /= m;
+    relu_mean[h] /= m;
   }
   orc_topk(seed_s, seeds, ns, K, seed_top, seed_top_s);
   const double tau = seed_top_s[K - 1];

@@ -7,16 +7,19 @@
 //               [0, c) and top-rep_topk'd; key occurrence counts; seeds =
 //               n_seeds keys of [0, c) by (count desc, key asc), kept in
 //               ascending key order (section 4).  A caller prior replaces it.
-//   seed pass   every row x every seed with the shared score micro-kernel,
-//               plus per-head activation counts and ReLU sums; seed top-K by
-//               (score desc, key asc); tau = its K-th score (section 2.1).
+//   seed pass   every row x every seed with the shared score micro-kernel;
+//               seed top-K by (score desc, key asc); tau = its K-th score
+//               (section 2.1).  Before it, per-head activation counts and
+//               ReLU sums over a sample of 128 seeds evenly spaced in seed
+//               order (section 4: activation patterns from 128 positions of
+//               the seed region).
 //   plan        per row: kept heads = the kept_heads largest
-//               |w_h| * mean_seeds max(x_h, 0); each omitted positive head
+//               |w_h| * mean_sample max(x_h, 0); each omitted positive head
 //               anchors on the kept head of smallest residual under the
 //               clamped projection beta = max(0, q_h.q_j/|q_j|^2) (section
 //               3.1); folded weights w'_j = w_j + sum beta_h w_h; residual
 //               R = sum w_h |d_h|; omitted negative heads active on at least
-//               neg_active_frac of the seeds aggregate into a_A = sum |w_h| q_h
+//               neg_active_frac of the sample aggregate into a_A = sum |w_h| q_h
 //               (section 3.2), carried in bf16 as a_hat.  All in fp64.
 //   bound       MFMA over the 32-row plan tile (kept heads, a_hat, zeros):
 //               U = sum w'_j max(x_j,0) - max(a_hat.k, 0) + C_r |k|; a key
@@ -28,7 +31,11 @@
 //               128 exact products err by at most ~2^-16 |q||k|).  So U is
 //               at least the score this device computes.
 //   compact     ballot bitmap -> ascending survivor ids; more than
-//               survivor_capacity sends the row to the exact path.
+//               survivor_capacity sends the row to the exact path.  The
+//               bound scan keeps a running survivor count per row and
+//               skips the rest of a row once it passes the capacity (the
+//               exact path will score every key of it anyway); the count
+//               then decides the row's fallback.
 //               With shared streams (section 4's compaction variant): rows
 //               go in groups of 4; a key that survives for at least 2 of
 //               the group's rows and lies in the group's common visible
@@ -61,13 +68,25 @@ struct DosaCtx {
 };
 
 struct DosaLayout {
-  size_t ctx, rep_q, rep_w, rep_vis, rep_scores, rep_ids, counts, seeds, seed_mask, seed_keys,
+  size_t ctx, rep_q, rep_w, rep_vis, rep_scores, rep_ids, counts, seeds, seed_mask, seed_keys, sample_keys,
       seed_scores, stat_cnt, stat_sum, top_idx, top_score, plan_a, plan_w, plan_c, knorm, bitmap,
-      surv_ids, surv_cnt, row_fb, kept_score, kept_id, kept_cnt, fb_list, fb_scores, shared_ids,
+      surv_ids, surv_cnt, bound_cnt, row_fb, kept_score, kept_id, kept_cnt, fb_list, fb_scores, shared_ids,
       shared_cnt, solo_cnt, shared_n, topk_ws, topk_ws_bytes, total;
 };
 
 static size_t au(size_t x) { return (x + 255) / 256 * 256; }
+
+// Activation statistics sample: 128 seeds (all of them when there are
+// fewer), evenly spaced in seed order (DoSA reading notes, section 4: the
+// planner counts activation patterns over 128 positions of the seed region).
+constexpr int kStatSample = 128;
+__host__ __device__ inline int stat_sample_size(int n_seeds) {
+  return n_seeds < kStatSample ? n_seeds : kStatSample;
+}
+// Seed index of sample i of m: round(i (n_seeds - 1) / (m - 1)), halves up.
+__host__ __device__ inline int stat_sample_index(int i, int m, int n_seeds) {
+  return m > 1 ? (int)((2LL * i * (n_seeds - 1) + (m - 1)) / (2LL * (m - 1))) : 0;
+}
 
 static DosaLayout dosa_layout(int32_t n_q, int32_t H, int32_t D, int64_t n_k, int32_t topk,
                               const si_dosa_params* p) {
@@ -91,6 +110,7 @@ static DosaLayout dosa_layout(int32_t n_q, int32_t H, int32_t D, int64_t n_k, in
   L.seeds = take(ns * 4);
   L.seed_mask = take(words * 4);
   L.seed_keys = take(ns * D * 2);
+  L.sample_keys = take((size_t)kStatSample * D * 2);
   L.seed_scores = take(nq * ns * 4);
   L.stat_cnt = take(nq * H * 4);
   L.stat_sum = take(nq * H * 4);
@@ -103,6 +123,7 @@ static DosaLayout dosa_layout(int32_t n_q, int32_t H, int32_t D, int64_t n_k, in
   L.bitmap = take(nq * words * 4);
   L.surv_ids = take(nq * cap * 4);
   L.surv_cnt = take(nq * 4);
+  L.bound_cnt = take(nq * 4);
   L.row_fb = take(nq * 4);
   L.kept_score = take(nq * cap * 4);
   L.kept_id = take(nq * cap * 4);
@@ -287,13 +308,30 @@ __global__ __launch_bounds__(256) void dosa_gather_seed_keys(const DosaCtx* ctx,
   }
 }
 
+__global__ __launch_bounds__(256) void dosa_gather_sample(const DosaCtx* ctx, const uint16_t* k,
+                                                          const int32_t* seeds, int n_seeds,
+                                                          int D, uint16_t* sample_keys) {
+  if (ctx->global_fallback) return;
+  const int m = stat_sample_size(n_seeds);
+  const int cpk = D / 8;  // 16-byte chunks per key
+  for (int e = threadIdx.x; e < m * cpk; e += 256) {
+    const int i = e / cpk, c = e % cpk;
+    const int j = seeds[stat_sample_index(i, m, n_seeds)];
+    reinterpret_cast<u32x4*>(sample_keys + (int64_t)i * D)[c] =
+        reinterpret_cast<const u32x4*>(k + (int64_t)j * D)[c];
+  }
+}
+
 // Seed scoring: every row against every seed key (dense [n_seeds, D] tile
-// source), the shared micro-kernel, plus per-head activation statistics.
+// source) with the shared micro-kernel.  Before it, the per-head activation
+// statistics of the row over the 128-seed sample (dense [n_sample, D]): the
+// count of x_h > 0 and the sum of max(x_h, 0).
 template <int MT, int KS, int QPW>
 __global__ __launch_bounds__(256, 2) void dosa_seed_score(
     const DosaCtx* ctx, const uint16_t* __restrict__ q, const uint16_t* __restrict__ sk,
-    const float* __restrict__ w, int64_t w_stride, int n_q, int H, int n_seeds,
-    float* __restrict__ seed_scores, int32_t* __restrict__ stat_cnt, float* __restrict__ stat_sum) {
+    const uint16_t* __restrict__ smp, int n_sample, const float* __restrict__ w,
+    int64_t w_stride, int n_q, int H, int n_seeds, float* __restrict__ seed_scores,
+    int32_t* __restrict__ stat_cnt, float* __restrict__ stat_sum) {
   constexpr int D = 16 * KS;
   constexpr int ROWB = D * 2 + 16;
   constexpr int CPK = D * 2 / 16;
@@ -308,55 +346,107 @@ __global__ __launch_bounds__(256, 2) void dosa_seed_score(
     }
     return;
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_index();
   const int r0 = (int)blockIdx.x * 4 * QPW + wave * QPW;
 
   bf16x8 a[QPW][MT][KS];
   float wv[QPW][MT][16];
-  int cnt[QPW][MT][16];
-  float rs[QPW][MT][16];
 #pragma unroll
   for (int i = 0; i < QPW; ++i) {
     load_q_frag<MT, KS>(q, r0 + i, H, r0 + i < n_q, a[i]);
     load_w_frag<MT>(w, w_stride, r0 + i, H, r0 + i < n_q, wv[i]);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        cnt[i][mt][v] = 0;
-        rs[i][mt][v] = 0.0f;
-      }
   }
-  const int ntiles = (n_seeds + 31) / 32;
   static_assert(CHUNKS % 256 == 0, "every thread stages whole chunks");
-  // seed keys through a buffer resource (zero past n_seeds, no branch
-  // around a load)
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)sk, (short)0, n_seeds * D * 2, 0x00020000);
   u32x4 pre[CPT];
-  auto fetch = [&](int t) {
+  // 32-key tiles of a dense key array through a buffer resource (zero past
+  // its n keys, no branch around a load), double buffered in LDS; body(t,
+  // brow) consumes tile t of the key array
+  auto stream = [&](const uint16_t* keys, int n, auto body) {
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)keys, (short)0, n * D * 2, 0x00020000);
+    auto fetch = [&](int t) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c)
-      pre[c] = __builtin_amdgcn_raw_buffer_load_b128(
-          krs, t * (32 * D * 2) + ((int)threadIdx.x + 256 * c) * 16, 0, 0);
-  };
-  auto stash = [&](int buf) {
+      for (int c = 0; c < CPT; ++c)
+        pre[c] = __builtin_amdgcn_raw_buffer_load_b128(
+            krs, t * (32 * D * 2) + ((int)threadIdx.x + 256 * c) * 16, 0, 0);
+    };
+    auto stash = [&](int buf) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      int ch = threadIdx.x + 256 * c;
-      int key = ch / CPK, part = ch % CPK;
-      *reinterpret_cast<u32x4*>(&lds[buf][key * ROWB + part * 16]) = pre[c];
+      for (int c = 0; c < CPT; ++c) {
+        int ch = threadIdx.x + 256 * c;
+        int key = ch / CPK, part = ch % CPK;
+        *reinterpret_cast<u32x4*>(&lds[buf][key * ROWB + part * 16]) = pre[c];
+      }
+    };
+    const int ntiles = (n + 31) / 32;
+    __syncthreads();  // the buffers' previous contents are consumed
+    fetch(0);
+    stash(0);
+    wait_memory();
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const int buf = t & 1;
+      fetch(t + 1 < ntiles ? t + 1 : t);  // the last one is a harmless repeat
+      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
+      body(t, &lds[buf][(lane & 31) * ROWB + (lane >> 5) * 16]);
+      // buffer buf ^ 1 held tile t - 1, read before the previous barrier
+      stash(buf ^ 1);
+      __syncthreads();
     }
   };
-  fetch(0);
-  stash(0);
-  wait_memory();
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    fetch(t + 1 < ntiles ? t + 1 : t);  // the last one is a harmless repeat
-    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
-    const unsigned char* brow = &lds[buf][(lane & 31) * ROWB + (lane >> 5) * 16];
+
+  {  // activation statistics over the sample (padding keys are zero: x = 0
+     // adds nothing to either statistic)
+    int cnt[QPW][MT][16];
+    float rs[QPW][MT][16];
+#pragma unroll
+    for (int i = 0; i < QPW; ++i)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          cnt[i][mt][v] = 0;
+          rs[i][mt][v] = 0.0f;
+        }
+    stream(smp, n_sample, [&](int t, const unsigned char* brow) {
+      (void)t;
+      f32x16 acc[QPW][MT];
+      mfma_tiles<QPW, MT, KS>(
+          a, [&](int s) { return as_bf16x8(*reinterpret_cast<const u32x4*>(brow + 32 * s)); },
+          acc);
+#pragma unroll
+      for (int i = 0; i < QPW; ++i)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float x = relu(acc[i][mt][v]);
+            cnt[i][mt][v] += x > 0.0f ? 1 : 0;
+            rs[i][mt][v] += x;
+          }
+    });
+    // reduce over the 32 key lanes of each half-wave
+#pragma unroll
+    for (int i = 0; i < QPW; ++i)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          int c = cnt[i][mt][v];
+          float f = rs[i][mt][v];
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) {
+            c += __shfl_xor(c, o, 64);
+            f += __shfl_xor(f, o, 64);
+          }
+          int h = mt * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if ((lane & 31) == 0 && r0 + i < n_q && h < H) {
+            stat_cnt[(int64_t)(r0 + i) * H + h] = c;
+            stat_sum[(int64_t)(r0 + i) * H + h] = f;
+          }
+        }
+  }
+  stream(sk, n_seeds, [&](int t, const unsigned char* brow) {
     f32x16 acc[QPW][MT];
     mfma_tiles<QPW, MT, KS>(
         a, [&](int s) { return as_bf16x8(*reinterpret_cast<const u32x4*>(brow + 32 * s)); },
@@ -364,44 +454,11 @@ __global__ __launch_bounds__(256, 2) void dosa_seed_score(
     const int j = t * 32 + (lane & 31);
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
-      float s = head_reduce<MT>(acc[i], wv[i]);
-      // padding keys are zero: x = 0 adds nothing to either statistic (the
-      // ReLU is the one the head sum took)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float x = relu(acc[i][mt][v]);
-          cnt[i][mt][v] += x > 0.0f ? 1 : 0;
-          rs[i][mt][v] += x;
-        }
+      const float sc = head_reduce<MT>(acc[i], wv[i]);
       if (lane < 32 && r0 + i < n_q && j < n_seeds)
-        seed_scores[(int64_t)(r0 + i) * n_seeds + j] = s;
+        seed_scores[(int64_t)(r0 + i) * n_seeds + j] = sc;
     }
-    // buffer buf ^ 1 held tile t - 1, read before the previous barrier
-    stash(buf ^ 1);
-    __syncthreads();
-  }
-  // reduce the statistics over the 32 key lanes of each half-wave
-#pragma unroll
-  for (int i = 0; i < QPW; ++i)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        int c = cnt[i][mt][v];
-        float f = rs[i][mt][v];
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) {
-          c += __shfl_xor(c, o, 64);
-          f += __shfl_xor(f, o, 64);
-        }
-        int h = mt * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if ((lane & 31) == 0 && r0 + i < n_q && h < H) {
-          stat_cnt[(int64_t)(r0 + i) * H + h] = c;
-          stat_sum[(int64_t)(r0 + i) * H + h] = f;
-        }
-      }
+  });
 }
 
 __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
@@ -422,108 +479,146 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
 }
 
 // Per-row plan (fp64).  One workgroup per row.  q_h rows sit in LDS as
-// floats (bf16 values are exact there) with a padded stride, so per-head
-// loops over d hit distinct banks; every dot product and sum is taken in
-// fp64 in increasing index order.
+// floats (bf16 values are exact there), 16-byte aligned.  Every per-head sum
+// over d is split over TPH threads of the head (chunks of D / TPH, each
+// summed in increasing d) and combined by a fixed butterfly, so the row's
+// plan is the same bits on every run; no order matters for soundness, which
+// the 2^-10 margin in C_r carries.
 constexpr int kPlanThreads = 256;
-constexpr int kPlanStride = 128 + 1;  // floats per q_h row in LDS
+constexpr int kPlanStride = 128 + 4;  // floats per q_h row in LDS
+__device__ __forceinline__ double sum_lanes(double x, int width) {
+  for (int o = 1; o < width; o <<= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
 __global__ __launch_bounds__(kPlanThreads) void dosa_plan(
     const DosaCtx* ctx, const uint16_t* __restrict__ q, const float* __restrict__ w,
-    int64_t w_stride, int H, int D, int n_seeds, int kept_heads, float neg_frac,
+    int64_t w_stride, int H, int D, int n_stat, int kept_heads, float neg_frac,
     const int32_t* __restrict__ stat_cnt, const float* __restrict__ stat_sum,
     uint16_t* __restrict__ plan_a, float* __restrict__ plan_w, float* __restrict__ plan_c) {
-  __shared__ float qf[64 * kPlanStride];
-  __shared__ double gdot[64][32];  // q_h . q_j for omitted h, kept index t
+  __shared__ __attribute__((aligned(16))) float qf[64 * kPlanStride];
+  __shared__ double gdot[64][32];  // q_h . q_j for omitted positive h, kept index t
   __shared__ double qq[64], wf[64], dn[64], beta[64], agg[128], part[2][128];
-  __shared__ float imp[64];
-  __shared__ int role[64], anchor[64], kept_list[32];
-  __shared__ int n_kept;
+  __shared__ float imp[64], wrow[64];
+  __shared__ int role[64], anchor[64], kept_list[32], pos_list[64];
+  __shared__ int n_kept, n_pos;
+  __shared__ double fin[5];
   if (ctx->global_fallback) return;
-  const int r = blockIdx.x, tid = threadIdx.x;
-  auto qv = [&](int h, int d) { return (double)qf[h * kPlanStride + d]; };
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  // TPH threads per head (H <= 64): head tid / TPH, d chunk tid % TPH
+  const int TPH = H <= 16 ? 16 : (H <= 32 ? 8 : 4);
+  const int hh = tid / TPH, cc = tid % TPH, dlen = D / TPH, d0 = cc * dlen;
   for (int e = tid; e < H * D; e += kPlanThreads)
     qf[(e / D) * kPlanStride + e % D] = __uint_as_float((uint32_t)q[(int64_t)r * H * D + e] << 16);
-  for (int h = tid; h < H; h += kPlanThreads)
-    imp[h] = fabsf(w[(int64_t)r * w_stride + h]) * (stat_sum[(int64_t)r * H + h] / (float)n_seeds);
+  for (int h = tid; h < H; h += kPlanThreads) {
+    wrow[h] = w[(int64_t)r * w_stride + h];
+    imp[h] = fabsf(wrow[h]) * (stat_sum[(int64_t)r * H + h] / (float)n_stat);
+  }
   __syncthreads();
+  const float* qh_ = &qf[hh * kPlanStride];
+  {  // |q_h|^2
+    double s0 = 0.0, s1 = 0.0;
+    for (int d = d0; d < d0 + dlen; d += 2) {
+      const double x0 = qh_[d], x1 = qh_[d + 1];
+      s0 += x0 * x0;
+      s1 += x1 * x1;
+    }
+    const double s = sum_lanes(s0 + s1, TPH);
+    if (cc == 0 && hh < H) qq[hh] = s;
+  }
   if (tid < H) {
     int h = tid, rank = 0;
     for (int g = 0; g < H; ++g)
       rank += (imp[g] > imp[h] || (imp[g] == imp[h] && g < h)) ? 1 : 0;
-    double s = 0.0;
-    for (int d = 0; d < D; ++d) s += qv(h, d) * qv(h, d);
-    qq[h] = s;
-    const float wh = w[(int64_t)r * w_stride + h];
-    const float act = (float)stat_cnt[(int64_t)r * H + h] / (float)n_seeds;
+    const float wh = wrow[h];
+    const float act = (float)stat_cnt[(int64_t)r * H + h] / (float)n_stat;
     role[h] = rank < kept_heads ? 1 : (wh > 0.0f ? 2 : (wh < 0.0f ? (act >= neg_frac ? 3 : 4) : 0));
   }
   __syncthreads();
-  if (tid == 0) {
-    int n = 0;
-    for (int h = 0; h < H; ++h)
-      if (role[h] == 1) kept_list[n++] = h;
-    n_kept = n;
-  }
-  __syncthreads();
-  const int nk = n_kept;
-  // dot products of omitted positive heads with every kept head, one
-  // (head, kept) pair per thread
-  for (int e = tid; e < H * nk; e += kPlanThreads) {
-    const int h = e / nk, t = e % nk;
-    if (role[h] == 2) {
-      const int j = kept_list[t];
-      double g = 0.0;
-      for (int d = 0; d < D; ++d) g += qv(h, d) * qv(j, d);
-      gdot[h][t] = g;
+  if (tid < 64) {  // kept heads and omitted positive heads, ascending
+    const bool kept = lane < H && role[lane] == 1, pos = lane < H && role[lane] == 2;
+    const uint64_t km = __ballot(kept), pm = __ballot(pos);
+    const uint64_t below = (1ull << lane) - 1ull;
+    if (kept) kept_list[__popcll(km & below)] = lane;
+    if (pos) pos_list[__popcll(pm & below)] = lane;
+    if (lane == 0) {
+      n_kept = __popcll(km);
+      n_pos = __popcll(pm);
     }
   }
   __syncthreads();
-  // anchors of omitted positive heads: smallest residual, lower head on ties
+  const int nk = n_kept, np = n_pos;
+  // q_h . q_j for every omitted positive head h and kept head j
+  for (int e = tid; e < np * nk; e += kPlanThreads) {
+    const int h = pos_list[e / nk], j = kept_list[e % nk];
+    const float4* a4 = reinterpret_cast<const float4*>(&qf[h * kPlanStride]);
+    const float4* b4 = reinterpret_cast<const float4*>(&qf[j * kPlanStride]);
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    for (int d = 0; d < D / 4; ++d) {
+      const float4 x = a4[d], y = b4[d];
+      s0 += (double)x.x * (double)y.x;
+      s1 += (double)x.y * (double)y.y;
+      s2 += (double)x.z * (double)y.z;
+      s3 += (double)x.w * (double)y.w;
+    }
+    gdot[h][e % nk] = (s0 + s1) + (s2 + s3);
+  }
+  __syncthreads();
+  // anchor of each omitted positive head: the kept head of smallest
+  // residual under the clamped projection, the lower head on ties
   if (tid < H) {
-    int h = tid;
+    const int h = tid;
     anchor[h] = -1;
     beta[h] = 0.0;
-    dn[h] = 0.0;
     if (role[h] == 2) {
       double best = INFINITY, bb = 0.0;
       int bj = -1;
       for (int t = 0; t < nk; ++t) {
-        int j = kept_list[t];
-        double g = gdot[h][t];
-        double b = qq[j] > 0.0 ? g / qq[j] : 0.0;
-        b = b < 0.0 ? 0.0 : b;
-        double r2 = qq[h] - 2.0 * b * g + b * b * qq[j];
+        const int j = kept_list[t];
+        const double g = gdot[h][t];
+        double bt = qq[j] > 0.0 ? g / qq[j] : 0.0;
+        bt = bt < 0.0 ? 0.0 : bt;
+        const double r2 = qq[h] - 2.0 * bt * g + bt * bt * qq[j];
         if (r2 < best) {
           best = r2;
-          bb = b;
+          bb = bt;
           bj = j;
         }
       }
-      double s = 0.0;  // explicit |q_h - beta q_a|: no cancellation in the bound
-      for (int d = 0; d < D; ++d) {
-        double e = qv(h, d) - (bj >= 0 ? bb * qv(bj, d) : 0.0);
-        s += e * e;
-      }
       anchor[h] = bj;
       beta[h] = bb;
-      dn[h] = sqrt(s);
     }
   }
   __syncthreads();
+  {  // |q_h - beta q_a| taken explicitly (no cancellation in the bound)
+    const int a = hh < H ? anchor[hh] : -1;
+    const double bb = hh < H ? beta[hh] : 0.0;
+    double s0 = 0.0, s1 = 0.0;
+    if (hh < H && role[hh] == 2) {
+      const float* qa = &qf[(a >= 0 ? a : 0) * kPlanStride];
+      for (int d = d0; d < d0 + dlen; d += 2) {
+        const double e0 = (double)qh_[d] - (a >= 0 ? bb * (double)qa[d] : 0.0);
+        const double e1 = (double)qh_[d + 1] - (a >= 0 ? bb * (double)qa[d + 1] : 0.0);
+        s0 += e0 * e0;
+        s1 += e1 * e1;
+      }
+    }
+    const double s = sum_lanes(s0 + s1, TPH);
+    if (cc == 0 && hh < H) dn[hh] = role[hh] == 2 ? sqrt(s) : 0.0;
+  }
   if (tid < H) {
-    int j = tid;
+    const int j = tid;
     double f = 0.0;
     if (role[j] == 1) {
-      f = (double)w[(int64_t)r * w_stride + j];
+      f = (double)wrow[j];
       for (int h = 0; h < H; ++h)
-        if (role[h] == 2 && anchor[h] == j) f += (double)w[(int64_t)r * w_stride + h] * beta[h];
+        if (role[h] == 2 && anchor[h] == j) f += (double)wrow[h] * beta[h];
     }
     wf[j] = f;
   }
   for (int d = tid; d < D; d += kPlanThreads) {
     double s = 0.0;
     for (int h = 0; h < H; ++h)
-      if (role[h] == 3) s += fabs((double)w[(int64_t)r * w_stride + h]) * qv(h, d);
+      if (role[h] == 3) s += fabs((double)wrow[h]) * (double)qf[h * kPlanStride + d];
     agg[d] = s;
     // the aggregate's bf16 carrier and its rounding error, per d
     const double ah = (double)__uint_as_float((uint32_t)f64_to_bf16_rne(s) << 16);
@@ -545,19 +640,41 @@ __global__ __launch_bounds__(kPlanThreads) void dosa_plan(
     else if (tid == nk) v = -1.0f;
     plan_w[(int64_t)r * 32 + tid] = v;
   }
+  // the margin scalar's sums: over heads in wave 0, over d in wave 1
+  if (tid < 64) {
+    const int h = lane;
+    double nw = 0.0, R = 0.0, nwf = 0.0;
+    if (h < H) {
+      const double wh = (double)wrow[h], n = sqrt(qq[h]);
+      nw = fabs(wh) * n;
+      R = role[h] == 2 ? wh * dn[h] : 0.0;
+      nwf = role[h] == 1 ? fabs(wf[h]) * n : 0.0;
+    }
+    nw = sum_lanes(nw, 64);
+    R = sum_lanes(R, 64);
+    nwf = sum_lanes(nwf, 64);
+    if (lane == 0) {
+      fin[0] = nw;
+      fin[1] = R;
+      fin[2] = nwf;
+    }
+  } else if (tid < 128) {
+    double e2 = 0.0, a2 = 0.0;
+    for (int d = lane; d < D; d += 64) {
+      e2 += part[0][d];
+      a2 += part[1][d];
+    }
+    e2 = sum_lanes(e2, 64);
+    a2 = sum_lanes(a2, 64);
+    if (lane == 0) {
+      fin[3] = e2;
+      fin[4] = a2;
+    }
+  }
+  __syncthreads();
   if (tid == 0) {
-    double R = 0.0, nw = 0.0, nwf = 0.0, err2 = 0.0, ah2 = 0.0;
-    for (int h = 0; h < H; ++h) {
-      double wh = (double)w[(int64_t)r * w_stride + h];
-      nw += fabs(wh) * sqrt(qq[h]);
-      if (role[h] == 2) R += wh * dn[h];
-      if (role[h] == 1) nwf += fabs(wf[h]) * sqrt(qq[h]);
-    }
-    for (int d = 0; d < D; ++d) {
-      err2 += part[0][d];
-      ah2 += part[1][d];
-    }
-    double err = sqrt(err2), ahn = sqrt(ah2);
+    const double nw = fin[0], R = fin[1], nwf = fin[2];
+    const double err = sqrt(fin[3]), ahn = sqrt(fin[4]);
     double C = R + err + 0x1p-10 * (nw + nwf + ahn + R + err);
     plan_c[r] = __double2float_ru(C);
   }
@@ -584,7 +701,8 @@ __global__ __launch_bounds__(256, 2) void dosa_bound(
     const float* __restrict__ plan_c, const float* __restrict__ top_score, int topk,
     const uint16_t* __restrict__ k, const float* __restrict__ knorm,
     const uint32_t* __restrict__ seed_mask, const int32_t* __restrict__ vis_len, int n_q,
-    int64_t n_k, uint32_t* __restrict__ bitmap, int64_t words, int nseg, int64_t seg_keys) {
+    int64_t n_k, uint32_t* __restrict__ bitmap, int64_t words, int nseg, int64_t seg_keys,
+    int32_t* __restrict__ bound_cnt, int cap) {
   constexpr int D = 16 * KS;
   constexpr int QB = 4 * QPW;
   constexpr int ROWB = D * 2 + 16;
@@ -592,8 +710,9 @@ __global__ __launch_bounds__(256, 2) void dosa_bound(
   constexpr int CHUNKS = 32 * CPK;
   constexpr int CPT = (CHUNKS + 255) / 256;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][32 * ROWB];
+  __shared__ int wdone[2][4];  // per tile parity: the wave has nothing left to scan
   if (ctx->global_fallback) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_index();
   int g;
   int64_t key_lo, key_hi;
   if (!segment_of((n_q + QB - 1) / QB, nseg, seg_keys, n_k, true, &g, &key_lo, &key_hi)) return;
@@ -654,10 +773,39 @@ __global__ __launch_bounds__(256, 2) void dosa_bound(
                                        nrs, (t * 32 + (lane & 31)) * 4, 0, 0));
     sw = __builtin_amdgcn_raw_buffer_load_b32(mrs, t * 4, 0, 0);
   };
+  // Survivor counts of the wave's rows: the count of every workgroup that
+  // scans them, in bound_cnt (read at the start and every kFlush tiles, past
+  // the L1), plus this wave's own since its last flush.  A row with more
+  // survivors than the capacity takes the exact path (its compaction reads
+  // the count, not the bitmap), so its remaining tiles need no bound; once
+  // no row of the workgroup needs one, the scan ends.  Every survivor is
+  // flushed into bound_cnt before the workgroup ends.
+  constexpr int kFlush = 16;
+  int seen[QPW], mine[QPW];
+  auto refresh = [&]() {
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      const int r = r0 + wave * QPW + i;
+      seen[i] = r < n_q ? __hip_atomic_load(&bound_cnt[r], __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT)
+                        : 0;
+    }
+  };
+  auto flush = [&]() {
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      const int r = r0 + wave * QPW + i;
+      if (lane == 0 && r < n_q && mine[i] > 0) atomicAdd(&bound_cnt[r], mine[i]);
+      mine[i] = 0;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) mine[i] = 0;
   float kn_n;
   uint32_t sw_n;
   fetch(t_lo);
   side(t_lo, kn_n, sw_n);
+  refresh();
   stash(t_lo & 1);
   wait_memory();
   __syncthreads();
@@ -670,7 +818,15 @@ __global__ __launch_bounds__(256, 2) void dosa_bound(
     side(tn, kn_n, sw_n);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the MFMAs
     const int64_t j = (int64_t)t * 32 + (lane & 31);
-    if (sw == 0xFFFFFFFFu) {
+    bool done = true;  // (uniform) no row of this wave needs this tile or a later one
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      const int r = r0 + wave * QPW + i;
+      done = done && (r >= n_q || (int64_t)t * 32 >= vis[i] || seen[i] + mine[i] > cap);
+    }
+    if (done) {
+      // nothing to scan for this wave's rows
+    } else if (sw == 0xFFFFFFFFu) {
       // every key of the tile is a seed (the cold prior's low-index keys
       // mostly are): nothing survives, no bound to compute
 #pragma unroll
@@ -693,20 +849,30 @@ __global__ __launch_bounds__(256, 2) void dosa_bound(
         int r = r0 + wave * QPW + i;
         if (lane == 0 && r < n_q && (int64_t)t * 32 < vis[i])
           bitmap[(int64_t)r * words + t] = (uint32_t)m;
+        mine[i] += __popcll(m);
       }
+    }
+    if (lane == 0) wdone[buf][wave] = done ? 1 : 0;
+    if ((t - t_lo) % kFlush == kFlush - 1) {
+      flush();
+      refresh();
     }
     // buffer buf ^ 1 held tile t - 1, read before the previous barrier
     stash(buf ^ 1);
     __syncthreads();
+    // (wdone[buf] is rewritten two tiles on, after every wave has passed
+    // the next barrier and so has read it here)
+    if (wdone[buf][0] & wdone[buf][1] & wdone[buf][2] & wdone[buf][3]) break;
   }
+  flush();
 }
 
 // Bitmap -> ascending survivor ids (one workgroup per row).
 constexpr int kCompThreads = 256;
 __global__ __launch_bounds__(kCompThreads) void dosa_compact(
     const DosaCtx* ctx, const uint32_t* __restrict__ bitmap, int64_t words,
-    const int32_t* __restrict__ vis_len, int64_t n_k, int cap, int32_t* __restrict__ surv_ids,
-    int32_t* __restrict__ surv_cnt, int32_t* __restrict__ row_fb) {
+    const int32_t* __restrict__ vis_len, int64_t n_k, int cap, const int32_t* __restrict__ bound_cnt,
+    int32_t* __restrict__ surv_ids, int32_t* __restrict__ surv_cnt, int32_t* __restrict__ row_fb) {
   __shared__ int red[kCompThreads / 64 + 4];
   const int r = blockIdx.x;
   if (ctx->global_fallback) {
@@ -716,16 +882,19 @@ __global__ __launch_bounds__(kCompThreads) void dosa_compact(
     }
     return;
   }
+  // a row over the capacity may have tiles the bound scan skipped: its
+  // count decides, and its bitmap is not read
+  const int counted = bound_cnt[r];
+  const bool over = counted > cap;
   int64_t off;
   const int64_t v = visible_len(vis_len, nullptr, r, n_k, n_k, &off);
-  const int64_t nw = (v + 31) / 32;
+  const int64_t nw = over ? 0 : (v + 31) / 32;
   const int64_t per = (nw + kCompThreads - 1) / kCompThreads;
   const int64_t w0 = (int64_t)threadIdx.x * per;
   int mine = 0;
   for (int64_t i = w0; i < w0 + per && i < nw; ++i) mine += __popc(bitmap[(int64_t)r * words + i]);
   int total;
   int pos = block_excl_scan<kCompThreads>(mine, red, &total);
-  const bool over = total > cap;
   if (!over) {
     for (int64_t i = w0; i < w0 + per && i < nw; ++i) {
       uint32_t m = bitmap[(int64_t)r * words + i];
@@ -737,7 +906,7 @@ __global__ __launch_bounds__(kCompThreads) void dosa_compact(
     }
   }
   if (threadIdx.x == 0) {
-    surv_cnt[r] = total;
+    surv_cnt[r] = over ? counted : total;
     row_fb[r] = over ? 1 : 0;
   }
 }
@@ -816,6 +985,7 @@ constexpr int kGroupRows = 4;
 __global__ __launch_bounds__(kCompThreads) void dosa_compact_groups(
     const DosaCtx* ctx, const uint32_t* __restrict__ bitmap, int64_t words,
     const int32_t* __restrict__ vis_len, int n_q, int64_t n_k, int cap,
+    const int32_t* __restrict__ bound_cnt,
     int32_t* __restrict__ shared_ids, int32_t* __restrict__ shared_cnt,
     int32_t* __restrict__ surv_ids, int32_t* __restrict__ solo_cnt,
     int32_t* __restrict__ surv_cnt, int32_t* __restrict__ shared_n, int32_t* __restrict__ row_fb) {
@@ -845,18 +1015,23 @@ __global__ __launch_bounds__(kCompThreads) void dosa_compact_groups(
   }
   const int64_t per = (nw + kCompThreads - 1) / kCompThreads;
   const int64_t w0 = (int64_t)t * per;
-  // each row's survivors
+  // each row's survivors; a row over the capacity (its count, which may
+  // miss tiles the bound scan skipped, decides) takes the exact path and
+  // its bitmap is not read
+  bool over[kGroupRows];
+  int counted[kGroupRows];
+#pragma unroll
+  for (int i = 0; i < kGroupRows; ++i) {
+    counted[i] = i < nr ? bound_cnt[r0 + i] : 0;
+    over[i] = counted[i] > cap;
+  }
   int tot[kGroupRows] = {0, 0, 0, 0}, tot_total[kGroupRows];
   for (int64_t wi = w0; wi < w0 + per && wi < nw; ++wi)
 #pragma unroll
     for (int i = 0; i < kGroupRows; ++i)
-      if (wi < nwr[i]) tot[i] += __popc(bitmap[(int64_t)(r0 + i) * words + wi]);
-  bool over[kGroupRows];
+      if (!over[i] && wi < nwr[i]) tot[i] += __popc(bitmap[(int64_t)(r0 + i) * words + wi]);
 #pragma unroll
-  for (int i = 0; i < kGroupRows; ++i) {
-    (void)block_excl_scan<kCompThreads>(tot[i], red, &tot_total[i]);
-    over[i] = tot_total[i] > cap;
-  }
+  for (int i = 0; i < kGroupRows; ++i) (void)block_excl_scan<kCompThreads>(tot[i], red, &tot_total[i]);
   // the word's masks (rows taking the exact path contribute none), and the
   // shared part
   auto masks = [&](int64_t wi, uint32_t (&m)[kGroupRows]) -> uint32_t {
@@ -894,7 +1069,7 @@ __global__ __launch_bounds__(kCompThreads) void dosa_compact_groups(
   }
   if (t == 0) shared_cnt[g] = sh_total;
   if (t < nr) {
-    surv_cnt[r0 + t] = tot_total[t];
+    surv_cnt[r0 + t] = over[t] ? counted[t] : tot_total[t];
     solo_cnt[r0 + t] = over[t] ? 0 : so_total[t];
     shared_n[r0 + t] = over[t] ? 0 : tot_total[t] - so_total[t];
     row_fb[r0 + t] = over[t] ? 1 : 0;
@@ -1115,6 +1290,7 @@ static hipError_t run_dosa(const uint16_t* q, const uint16_t* k, const float* w,
   SI_TRY((fill_i32, dim3(grid_for(n_k, 256)), dim3(256), 0, st, I(L.counts), n_k, 0));
   SI_TRY((fill_i32, dim3(grid_for(words, 256)), dim3(256), 0, st, I(L.seed_mask), words, 0));
   SI_TRY((fill_i32, dim3(grid_for(n_q, 256)), dim3(256), 0, st, I(L.kept_cnt), (int64_t)n_q, 0));
+  SI_TRY((fill_i32, dim3(grid_for(n_q, 256)), dim3(256), 0, st, I(L.bound_cnt), (int64_t)n_q, 0));
   if (p->seed_ids == nullptr) {
     SI_TRY((dosa_gather_rep, dim3(R), dim3(256), 0, st, q, w, wst, n_q, H, D, R, U16(L.rep_q),
             F(L.rep_w)));
@@ -1139,10 +1315,13 @@ static hipError_t run_dosa(const uint16_t* q, const uint16_t* k, const float* w,
           I(L.seeds), reinterpret_cast<uint32_t*>(ws + L.seed_mask)));
   SI_TRY((dosa_gather_seed_keys, dim3(grid_for((int64_t)ns * (D / 8), 256)), dim3(256), 0, st,
           ctx, k, I(L.seeds), ns, D, U16(L.seed_keys)));
+  SI_TRY((dosa_gather_sample, dim3(1), dim3(256), 0, st, ctx, k, I(L.seeds), ns, D,
+          U16(L.sample_keys)));
   constexpr int QPW = MT == 1 ? 2 : 1;
+  const int n_stat = stat_sample_size(ns);
   SI_TRY(((dosa_seed_score<MT, KS, QPW>), dim3((n_q + 4 * QPW - 1) / (4 * QPW)), dim3(256), 0, st,
-          ctx, q, U16(L.seed_keys), w, wst, n_q, H, ns, F(L.seed_scores), I(L.stat_cnt),
-          F(L.stat_sum)));
+          ctx, q, U16(L.seed_keys), U16(L.sample_keys), n_stat, w, wst, n_q, H, ns,
+          F(L.seed_scores), I(L.stat_cnt), F(L.stat_sum)));
   {
     TopkArgs ta;
     ta.scores = F(L.seed_scores); ta.stride = ns; ta.vis_len = nullptr; ta.k_row_offset = nullptr;
@@ -1152,7 +1331,7 @@ static hipError_t run_dosa(const uint16_t* q, const uint16_t* k, const float* w,
     hipError_t e = launch_topk(ta, st);
     if (e != hipSuccess) return e;
   }
-  SI_TRY((dosa_plan, dim3(n_q), dim3(kPlanThreads), 0, st, ctx, q, w, wst, H, D, ns,
+  SI_TRY((dosa_plan, dim3(n_q), dim3(kPlanThreads), 0, st, ctx, q, w, wst, H, D, n_stat,
           p->kept_heads, p->neg_active_frac, I(L.stat_cnt), F(L.stat_sum), U16(L.plan_a),
           F(L.plan_w), F(L.plan_c)));
   SI_TRY((dosa_knorm, dim3(grid_for(n_k, 256)), dim3(256), 0, st, k, n_k, D, F(L.knorm)));
@@ -1162,19 +1341,20 @@ static hipError_t run_dosa(const uint16_t* q, const uint16_t* k, const float* w,
     SI_TRY(((dosa_bound<KS, 2>), dim3((unsigned)segment_grid((n_q + 7) / 8, nseg)), dim3(256), 0,
             st, ctx, U16(L.plan_a), F(L.plan_w), F(L.plan_c), F(L.top_score), topk, k,
             F(L.knorm), reinterpret_cast<const uint32_t*>(ws + L.seed_mask), vis, n_q, n_k,
-            reinterpret_cast<uint32_t*>(ws + L.bitmap), words, nseg, seg_keys));
+            reinterpret_cast<uint32_t*>(ws + L.bitmap), words, nseg, seg_keys, I(L.bound_cnt),
+            cap));
   }
   const bool groups = p->shared_streams != 0;
   const int n_groups = (n_q + kGroupRows - 1) / kGroupRows;
   if (groups) {
     SI_TRY((dosa_compact_groups, dim3(n_groups), dim3(kCompThreads), 0, st, ctx,
             reinterpret_cast<const uint32_t*>(ws + L.bitmap), words, vis, n_q, n_k, cap,
-            I(L.shared_ids), I(L.shared_cnt), I(L.surv_ids), I(L.solo_cnt), I(L.surv_cnt),
+            I(L.bound_cnt), I(L.shared_ids), I(L.shared_cnt), I(L.surv_ids), I(L.solo_cnt), I(L.surv_cnt),
             I(L.shared_n), I(L.row_fb)));
   } else {
     SI_TRY((dosa_compact, dim3(n_q), dim3(kCompThreads), 0, st, ctx,
             reinterpret_cast<const uint32_t*>(ws + L.bitmap), words, vis, n_k, cap,
-            I(L.surv_ids), I(L.surv_cnt), I(L.row_fb)));
+            I(L.bound_cnt), I(L.surv_ids), I(L.surv_cnt), I(L.row_fb)));
   }
   SI_TRY(((dosa_rescore<MT, KS>), dim3(n_q), dim3(256), 0, st, ctx, q, w, wst, H, k, F(L.top_score),
           topk, I(L.surv_ids), I(groups ? L.solo_cnt : L.surv_cnt), I(L.row_fb), cap,

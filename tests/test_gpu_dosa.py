@@ -95,6 +95,27 @@ def test_capacity_overflow_takes_exact_path():
     assert st["fallback"].sum() > 0
 
 
+@pytest.mark.parametrize("shared", [False, True])
+def test_capacity_early_stop(shared):
+    """The bound scan stops counting a row once it passes the capacity: the
+    fallback rows are exactly those whose full survivor count (taken with a
+    capacity no row reaches) exceeds it, their reported count is above it,
+    and every other row's count is exact."""
+    cfg = _small(True, seed=15, n_q=40, L=900, n_seeds=200)
+    say(f"dosa early stop shared={shared}")
+    _, _, _, _, full = _run_both(cfg, survivor_capacity=8192, shared_streams=shared)
+    exact = full["n_survivors"]
+    assert np.all(full["fallback"] == 0)
+    say(f"exact survivor counts {exact.min()}..{exact.max()}")
+    for cap in (1, int(np.median(exact)), int(exact.max())):
+        ui, us, di, ds, st = _run_both(cfg, survivor_capacity=cap, shared_streams=shared)
+        _assert_bit_exact(ui, us, di, ds)
+        fb = st["fallback"].astype(bool)
+        np.testing.assert_array_equal(fb, exact > cap)
+        assert np.all(st["n_survivors"][fb] > cap)
+        np.testing.assert_array_equal(st["n_survivors"][~fb], exact[~fb])
+
+
 def test_too_few_common_keys_falls_back():
     cfg = _small(True, seed=6)
     cfg["vis_len"] = cfg["vis_len"].copy()
