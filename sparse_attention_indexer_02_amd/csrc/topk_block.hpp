@@ -196,10 +196,12 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   // A. load.  A NaN score is taken as -inf (its order is unspecified; this
   //    makes every comparison below a total preorder on floats, -0 == +0).
   //    Every position is loaded through a buffer resource bounded at the
-  //    row's end, so a position past the end reads 0.  Those zeros take
-  //    part in the value range (which then covers 0 as well: still a valid
-  //    range, at worst a coarser one) and the registers are never
-  //    rewritten; only the bin counts and the selection mask them out.
+  //    row's end, so a position past the end reads 0.  In the partly
+  //    visible group row those zeros take part in the value range (which
+  //    then covers 0 as well: still a valid range, at worst a coarser one);
+  //    group rows wholly past the end are skipped by every per-item loop.
+  //    Only the bin counts and the selection mask out the positions past
+  //    the end.
 #pragma unroll
   for (int k = 0; k < kBins / (4 * kBT); ++k)
     *reinterpret_cast<uint4*>(&sm.bins[4 * t + 4 * kBT * k]) = make_uint4(0u, 0u, 0u, 0u);
@@ -251,10 +253,16 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   }
   float vlo = __builtin_inff(), vhi = -__builtin_inff();
 #pragma unroll
-  for (int i = 0; i < kBPer; ++i) {
-    x[i] = clean(x[i]);
-    vlo = __builtin_fminf(vlo, x[i]);
-    vhi = __builtin_fmaxf(vhi, x[i]);
+  for (int j = 0; j < kBGroups; ++j) {
+    if (j < gused) {  // (uniform) group rows past the end stay 0 and out of the range
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i = 4 * j + c;
+        x[i] = clean(x[i]);
+        vlo = __builtin_fminf(vlo, x[i]);
+        vhi = __builtin_fmaxf(vhi, x[i]);
+      }
+    }
   }
   {
     const uint32_t klo = __ockl_wfred_min_u32(order_key(vlo));
@@ -326,9 +334,13 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
   // the bins are computed once and kept packed, two per register
   uint32_t pk[kBPer / 2];
 #pragma unroll
-  for (int j = 0; j < kBPer / 2; ++j)
-    pk[j] = ((uint32_t)((x[2 * j] - vmin) * scale) |
-             ((uint32_t)((x[2 * j + 1] - vmin) * scale) << 16)) & keep_bins;
+  for (int j = 0; j < kBPer / 2; ++j) {
+    if (j / 2 < gused)
+      pk[j] = ((uint32_t)((x[2 * j] - vmin) * scale) |
+               ((uint32_t)((x[2 * j + 1] - vmin) * scale) << 16)) & keep_bins;
+    else
+      pk[j] = 0u;  // positions past the row: never counted or selected
+  }
   auto bin_of = [&](int i) -> uint32_t { return (pk[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu; };
 #pragma unroll
   for (int j = 0; j < kBGroups; ++j) {
@@ -413,7 +425,8 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
     // and adding each compare, highest item first: one add per item)
     uint32_t inb = 0u;
 #pragma unroll
-    for (int i = kBPer - 1; i >= 0; --i) inb = inb + inb + (uint32_t)((int)bin_of(i) == b1);
+    for (int i = kBPer - 1; i >= 0; --i)
+      inb = (i >> 2) < gused ? inb + inb + (uint32_t)((int)bin_of(i) == b1) : inb + inb;
     inb &= vm;
     if (in_bin <= kBrute) {
       // b1 holds few items: each holder walks its set bits, re-reading the
@@ -482,12 +495,14 @@ __device__ __forceinline__ void topk_row_block(const TopkArgs& a, int r, int cy,
     const int need_eq = K - n_gt;
     uint32_t gem = 0u;
 #pragma unroll
-    for (int i = kBPer - 1; i >= 0; --i) gem = gem + gem + (uint32_t)(x[i] >= thr);
+    for (int i = kBPer - 1; i >= 0; --i)
+      gem = (i >> 2) < gused ? gem + gem + (uint32_t)(x[i] >= thr) : gem + gem;
     selm = gem & vm;
     if (need_eq < n_eq) {  // uniform: T is tied past the K-th place
       uint32_t eqm = 0u;
 #pragma unroll
-      for (int i = kBPer - 1; i >= 0; --i) eqm = eqm + eqm + (uint32_t)(x[i] == thr);
+      for (int i = kBPer - 1; i >= 0; --i)
+        eqm = (i >> 2) < gused ? eqm + eqm + (uint32_t)(x[i] == thr) : eqm + eqm;
       eqm &= vm;
       const uint32_t gtm = selm & ~eqm;
       for (int i = t; i < kBN / 32; i += kBT) sm.x.eq.bits[i] = 0u;

@@ -57,7 +57,9 @@ __device__ __forceinline__ uint64_t seg_bit32(int32_t x, uint32_t L, uint32_t S,
 // the calling wave owns segment s (every lane of the wave calls it).
 __device__ __forceinline__ void write_witnesses(int32_t* row, uint64_t occ, uint32_t L,
                                                 uint32_t Se, int keep, int B) {
-  const int lane = threadIdx.x & 63;
+  // the lane id from the lane masks, so no copy of it computed earlier has
+  // to stay live until here (the fused top-K otherwise spills one)
+  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const bool empty = (uint32_t)lane < Se && !((occ >> lane) & 1ull);
   const uint64_t emask = __ballot(empty);
   if (empty) {
