@@ -530,13 +530,43 @@ def bench_dosa(args):
     return out
 
 
+def bench_topk_lengths(args):
+    """The top-K stage (rows_topk, K = 2048) on 8192 rows of N(0, 9) scores
+    with every row of one length, for several lengths, and with the causal
+    prefill's lengths 1..8192: how its time splits into a per-row part that
+    does not depend on the length and one that does."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_indexer_02_amd as si
+    R, N, K = 8192, 8192, 2048
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device="cpu").manual_seed(0)
+    scores = (torch.randn((R, N), generator=g) * 3.0).to(dev)
+    out = torch.empty((R, K), dtype=torch.int32, device=dev)
+    cases = [("causal 1..8192", torch.arange(1, R + 1, dtype=torch.int32))]
+    cases += [(f"all rows {n}", torch.full((R,), n, dtype=torch.int32))
+              for n in (256, 1024, 2048, 4096, 6144, 8192)]
+    res = {}
+    for name, vis in cases:
+        vis = vis.to(dev)
+        _, per = timed_steps([("topk", lambda: si.rows_topk(scores, vis, K, out_idx=out,
+                                                            want_scores=False))],
+                             args.steps, args.warmup)
+        res[name] = per["topk"]
+    return dict(metric="top-K stage time by row length (8192 rows, K 2048)", unit="ms",
+                ms=res, n_gpus=1, steps=args.steps, warmup=args.warmup, data="synthetic",
+                higher_is_better=False)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "decode", "dosa", "dosa_structured", "block"])
+                    choices=["prefill", "decode", "dosa", "dosa_structured", "block",
+                             "topk_lengths"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -564,6 +594,8 @@ def main():
     import synth
     if args.workload == "block":
         out = bench_block(args)
+    elif args.workload == "topk_lengths":
+        out = bench_topk_lengths(args)
     elif args.workload in ("dosa", "dosa_structured"):
         out = bench_dosa(args)
     else:
