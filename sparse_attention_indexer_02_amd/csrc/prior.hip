@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256) void prior_compact(
   __shared__ uint32_t wb[CW];
   __shared__ int wpre[CW];
   __shared__ int red[256 / 64 + 4];
-  const int r = blockIdx.x, t = threadIdx.x;
+  const int r = rows_grid_row(), t = threadIdx.x;
   const int64_t c = blockIdx.y;
   // the chunk's bitmap words and the row's chunk counts are read before the
   // row's length arrives (entries past it are masked below)

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256, 2) void score_mfma_rows(
   constexpr int ES = FP8 ? 1 : 2;        // bytes per key element
   constexpr int NL = FP8 ? KS / 2 : KS;  // 16-byte loads per lane per tile
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = blockIdx.x;
+  const int r = rows_grid_row();
   int64_t off;
   const int64_t v = visible_len(vis_len, row_off, r, n_k, max_vis, &off);
   const int64_t c0 = (int64_t)blockIdx.y * kRowsChunk;
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256, 3) void score_mfma_rows_fp8(
   __shared__ __attribute__((aligned(16))) unsigned char kbuf[4][NB][TB];
   __shared__ __attribute__((aligned(16))) float sbuf[4][NB][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = blockIdx.x;
+  const int r = rows_grid_row();
   int64_t off;
   const int64_t v = visible_len(vis_len, row_off, r, n_k, max_vis, &off);
   const int64_t c0 = (int64_t)blockIdx.y * kRowsChunk;

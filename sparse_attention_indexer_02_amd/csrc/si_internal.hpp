@@ -201,6 +201,17 @@ struct ScoreArgs {
 };
 // Keys per workgroup of the per-row (decode layout) score kernels.
 constexpr int64_t kRowsChunk = 4096;
+// Row of a workgroup in a (rows x chunks) grid over ragged rows.  Workgroups go
+// to the XCDs and their shader engines round robin in launch order, so with
+// the row as the fast grid index every engine would take a fixed subset of
+// the rows (all of their chunks), and ragged rows would leave engines idle
+// while others work through long rows.  Each chunk column rotates the rows by
+// its index instead, so a row's chunks spread over the engines.
+__device__ __forceinline__ int rows_grid_row() {
+  const unsigned n = gridDim.x;
+  return (int)((blockIdx.x + n - blockIdx.y % n) % n);
+}
+
 inline int64_t rows_key_chunks(int64_t max_vis) { return (max_vis + kRowsChunk - 1) / kRowsChunk; }
 hipError_t launch_score(const ScoreArgs& a, hipStream_t st);
 bool score_mfma_supported(const ScoreArgs& a);

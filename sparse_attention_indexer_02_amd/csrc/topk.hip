@@ -103,7 +103,8 @@ template <bool WIT, bool CHUNK>
 __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(8))) void topk_block(
     TopkArgs a) {
   __shared__ TopkSmem<kBT> S;
-  int r = (int)blockIdx.x;
+  // (a chunk pass's grid is rows x chunks: rotated as for the decode score)
+  int r = rows_grid_row();
   if (a.row_list) {
     if (r >= *a.row_count) return;
     r = a.row_list[r];
