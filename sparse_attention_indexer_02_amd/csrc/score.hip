@@ -308,6 +308,48 @@ __global__ __launch_bounds__(256) void score_generic(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// fp32 queries and keys: v_mfma_f32_32x32x2_f32 tiles with the same roles as
+// the bf16 path (heads on the MFMA rows, 32 keys on the columns, two d per
+// step: lane l supplies head l % 32, or key l % 32, at d = 2 s + l / 32),
+// and the same ReLU * w head sum (head_reduce), which the 32x32 accumulator
+// layout shares.  One wave per 32-key tile, four tiles of a row per
+// workgroup; the query fragments are read from the cache per step.
+// ---------------------------------------------------------------------------
+template <int MT>
+__global__ __launch_bounds__(256) void score_mfma_f32(ScoreArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = rows_grid_row();
+  int64_t off;
+  const int64_t v = visible_len(a.vis_len, a.k_row_offset, r, a.n_k, a.max_vis, &off);
+  const int64_t t0 = ((int64_t)blockIdx.y * 4 + wave) * 32;  // this wave's first key
+  if (t0 >= v) return;
+  const int H = a.H, D = a.D, hk = lane >> 5;
+  const int64_t key = t0 + (lane & 31);
+  const bool kvis = key < v;
+  // a key past the row is read as the tile's first key; its score is not stored
+  const float* krow = reinterpret_cast<const float*>(a.k) + (off + (kvis ? key : t0)) * D;
+  const float* qrow = reinterpret_cast<const float*>(a.q) + (int64_t)r * H * D;
+  float wv[MT][16];
+  load_w_frag<MT>(a.w, a.w_row_stride, r, H, true, wv);
+  f32x16 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[mt][e] = 0.0f;
+  for (int d = 0; d < D; d += 2) {
+    const float b = krow[d + hk];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int h = mt * 32 + (lane & 31);
+      const float av = h < H ? qrow[(int64_t)h * D + d + hk] : 0.0f;
+      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b, acc[mt], 0, 0, 0);
+    }
+  }
+  const float s = head_reduce<MT>(acc, wv);
+  if (lane < 32 && kvis) a.scores[(int64_t)r * a.score_stride + key] = s;
+}
+
+// ---------------------------------------------------------------------------
 // Dispatch.
 // ---------------------------------------------------------------------------
 bool score_mfma_supported(const ScoreArgs& a) {
@@ -379,6 +421,13 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t st) {
                      : launch_mfma<2, 8>(a, nullptr, nullptr, st);
     return MT == 1 ? launch_mfma<1, 4>(a, nullptr, nullptr, st)
                    : launch_mfma<2, 4>(a, nullptr, nullptr, st);
+  }
+  if (a.q_dtype == SI_F32 && a.k_dtype == SI_F32 && a.D % 2 == 0 && a.H >= 1 && a.H <= 64) {
+    const int64_t by = (a.max_vis + 127) / 128;  // four 32-key tiles per workgroup
+    const dim3 grid((unsigned)a.n_q, (unsigned)by);
+    if (a.H <= 32) hipLaunchKernelGGL(score_mfma_f32<1>, grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(score_mfma_f32<2>, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
   }
   const int64_t bx = (a.max_vis + 255) / 256;
   hipLaunchKernelGGL(score_generic, dim3((unsigned)a.n_q, (unsigned)bx), dim3(256), 0, st, a);

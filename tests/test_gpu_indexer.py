@@ -29,11 +29,36 @@ def _all_rows(orc, cfg):
 
 
 def test_tiny_fp32(orc):
+    """The tiny fp32 configuration (H4 D16): the fp32 MFMA score kernel."""
     _all_rows(orc, synth.tiny())
 
 
+@pytest.mark.parametrize("n_q,L,H,D,K", [(9, 301, 5, 24, 40), (37, 700, 40, 64, 100),
+                                         (20, 180, 64, 2, 33)])
+def test_fp32_mfma_shapes(orc, n_q, L, H, D, K):
+    """fp32 MFMA tiles with padded head rows (H 5, 40 -> two head tiles, 64),
+    D from 2 up, ragged causal rows with a partial last tile."""
+    _all_rows(orc, synth.tiny(seed=n_q, n_q=n_q, L=L, H=H, D=D, topk=K))
+
+
+def test_fp32_mfma_row_offsets(orc):
+    """fp32 per-row keys (row offsets, ragged lengths) through the fp32 MFMA
+    kernel's rotated (rows x tiles) grid."""
+    cfg = synth.tiny(seed=21, n_q=12, L=900, H=8, D=32, topk=64)
+    rng = np.random.default_rng(21)
+    lens = rng.integers(1, 400, cfg["n_q"]).astype(np.int32)
+    cfg["k_row_offset"] = (np.cumsum(lens) - lens).astype(np.int64)
+    cfg["k"] = rng.standard_normal((int(lens.sum()), cfg["D"]), dtype=np.float32)
+    cfg["n_k"] = int(lens.sum())
+    cfg["vis_len"] = lens
+    cfg["max_vis"] = int(lens.max())
+    cfg["name"] = "fp32 row offsets"
+    _all_rows(orc, cfg)
+
+
 def test_generic_fp32_odd_shape(orc):
-    _all_rows(orc, synth.tiny(seed=3, n_q=9, L=301, H=5, D=24, topk=40))
+    """Odd D stays on the generic VALU kernel."""
+    _all_rows(orc, synth.tiny(seed=3, n_q=9, L=301, H=5, D=23, topk=40))
 
 
 @pytest.mark.parametrize("n_q,L,H,D,K", [(300, 700, 64, 128, 128), (600, 600, 64, 128, 512),
