@@ -228,6 +228,15 @@ def bench_indexer(args, cfg, workload):
         roof = dict(bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=ach / PEAK_BF16_TFLOPS, traffic=counters_for(workload),
                     kernel="score_mfma_shared")
+    # the step's other passes against their own (HBM) bound, beside the
+    # dominant kernel's figure
+    roof["other_passes"] = {
+        "topk_block": dict(bound="hbm", achieved=kern["topk_stage"]["gbs"], peak=PEAK_HBM_GBS,
+                           unit="GB/s", frac=kern["topk_stage"]["hbm_frac"]),
+        "witness_merge": dict(bound="hbm", achieved=kern["witness"]["gbs"], peak=PEAK_HBM_GBS,
+                              unit="GB/s", frac=kern["witness"]["hbm_frac"],
+                              note="one launch between events"),
+    }
     step_ms = fz["step"]
     kern["two_calls"] = dict(ms=per["score_topk"] + per["witness"],
                              note="idx_score_topk then kvwitness_merge")
