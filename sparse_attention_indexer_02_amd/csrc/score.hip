@@ -1,7 +1,7 @@
 // Lightning-indexer score  s[r, j] = sum_h w[r, h] * max(q[r, h, :] . k[j, :], 0)
 // (DoSA reading notes, section 3), written for every visible key.
 //
-// Three kernels:
+// Kernels:
 //  * score_mfma_shared: bf16 q and bf16 keys shared by all rows (prefill).
 //    Heads sit in the MFMA row dimension (32x32x16 bf16 tiles), keys in
 //    the column dimension, D is the reduction.  A workgroup of 4 waves owns
@@ -9,11 +9,15 @@
 //    each key tile is read from L2 once per workgroup and feeds every query
 //    of it.  The ReLU * w head reduction runs in registers on the
 //    accumulator tile.  Optionally driven by a device row list.
-//  * score_mfma_rows: bf16 queries against per-row keys (decode layout),
-//    keys bf16 or OCP fp8 e4m3fn (converted exactly to bf16 in registers,
-//    per-token scale applied after the head sum: ReLU(c x) = c ReLU(x) for
-//    c > 0).  No reuse across rows, so keys go straight to registers.
-//  * score_generic: VALU fp32 path for fp32 inputs and shapes the MFMA
+//  * score_mfma_rows: bf16 queries against bf16 per-row keys (decode
+//    layout).  No reuse across rows, so keys go straight to registers.
+//  * score_mfma_rows_fp8: the same with OCP fp8 e4m3fn keys, staged through
+//    a per-wave LDS ring and converted exactly to bf16; the per-token scale
+//    is applied after the head sum (ReLU(c x) = c ReLU(x) for c > 0).
+//    Optionally filters the written scores by a per-row threshold.
+//  * score_mfma_f32: fp32 queries and keys on v_mfma_f32_32x32x2_f32 with
+//    the same accumulator layout and head sum.
+//  * score_generic: VALU fp32 path for the shapes and dtype mixes the MFMA
 //    kernels do not cover.
 #include "score_rows.hpp"
 #include "score_shared.hpp"
