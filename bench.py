@@ -568,6 +568,30 @@ def bench_topk_lengths(args):
                 higher_is_better=False)
 
 
+def bench_mfma_ref(args):
+    """The MFMA rate a vendor library reaches on this machine: bf16 GEMMs
+    through torch.matmul (hipBLASLt), large and square, so the score
+    kernel's fraction of the published peak can be read against what a
+    plain GEMM attains under the same power and clock limits."""
+    import torch
+    dev = torch.device("cuda", 0)
+    res = {}
+    for n in (4096, 8192, 16384):
+        g = torch.Generator(device="cpu").manual_seed(n)
+        a = torch.randn((n, n), generator=g).to(dev, torch.bfloat16)
+        b = torch.randn((n, n), generator=g).to(dev, torch.bfloat16)
+        c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+        steps = max(3, args.steps // (n // 4096) ** 2)
+        _, per = timed_steps([("mm", lambda: torch.matmul(a, b, out=c))], steps,
+                             max(2, args.warmup // 4))
+        tf = 2.0 * n ** 3 / per["mm"] / 1e9
+        res[f"{n}x{n}x{n}"] = dict(ms=per["mm"], tflops=tf, frac=tf / PEAK_BF16_TFLOPS)
+        del a, b, c
+    return dict(metric="bf16 GEMM rate of torch.matmul (hipBLASLt)", unit="TFLOP/s",
+                gemms=res, peak=PEAK_BF16_TFLOPS, n_gpus=1, data="synthetic",
+                higher_is_better=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -575,7 +599,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "decode", "dosa", "dosa_structured", "block",
-                             "topk_lengths"])
+                             "topk_lengths", "mfma_ref"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -605,6 +629,8 @@ def main():
         out = bench_block(args)
     elif args.workload == "topk_lengths":
         out = bench_topk_lengths(args)
+    elif args.workload == "mfma_ref":
+        out = bench_mfma_ref(args)
     elif args.workload in ("dosa", "dosa_structured"):
         out = bench_dosa(args)
     else:
