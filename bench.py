@@ -563,9 +563,14 @@ def bench_topk_lengths(args):
                                                             want_scores=False))],
                              args.steps, args.warmup)
         res[name] = per["topk"]
+    # reference: torch.topk (sorted) on the same full-length rows
+    vals = torch.empty((R, K), dtype=torch.float32, device=dev)
+    idx = torch.empty((R, K), dtype=torch.int64, device=dev)
+    _, per = timed_steps([("ref", lambda: torch.topk(scores, K, dim=1, sorted=True,
+                                                     out=(vals, idx)))], args.steps, args.warmup)
     return dict(metric="top-K stage time by row length (8192 rows, K 2048)", unit="ms",
-                ms=res, n_gpus=1, steps=args.steps, warmup=args.warmup, data="synthetic",
-                higher_is_better=False)
+                ms=res, torch_topk_all_rows_8192_ms=per["ref"], n_gpus=1, steps=args.steps,
+                warmup=args.warmup, data="synthetic", higher_is_better=False)
 
 
 def bench_mfma_ref(args):
