@@ -187,6 +187,10 @@ def bench_indexer(args, cfg, workload):
     WIT_REP = 8
     _, wt = timed_steps([("witness", lambda: [witness() for _ in range(WIT_REP)])], args.steps,
                         args.warmup)
+    # a plain device copy of the id rows the merge works on, one launch per
+    # event like the merge: the pages measure the merge against such a copy
+    row_copy = torch.empty_like(out_idx)
+    _, cp = timed_steps([("copy", lambda: row_copy.copy_(out_idx))], args.steps, args.warmup)
 
     flops = pairs * 2.0 * H * D
     kbytes = cfg["k"].nbytes + (cfg["k_scale"].nbytes if cfg["k_scale"] is not None else 0)
@@ -200,7 +204,8 @@ def bench_indexer(args, cfg, workload):
         "score_topk": dict(ms=per["score_topk"], tflops=flops / per["score_topk"] / 1e9,
                            algo_flops=flops),
         "witness": dict(ms=per["witness"], gbs=wit_bytes / per["witness"] / 1e6,
-                        algo_bytes=wit_bytes),
+                        algo_bytes=wit_bytes, row_copy_ms=cp["copy"],
+                        vs_row_copy=per["witness"] / cp["copy"]),
         "witness_stage": dict(ms=wt["witness"] / WIT_REP,
                               gbs=wit_bytes / (wt["witness"] / WIT_REP) / 1e6,
                               algo_bytes=wit_bytes, launches_per_event=WIT_REP),
