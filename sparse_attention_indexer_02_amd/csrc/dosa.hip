@@ -323,10 +323,14 @@ __global__ __launch_bounds__(256) void dosa_gather_sample(const DosaCtx* ctx, co
 }
 
 // Seed scoring: every row against every seed key (dense [n_seeds, D] tile
-// source) with the shared micro-kernel.  Before it, the per-head activation
-// statistics of the row over the 128-seed sample (dense [n_sample, D]): the
-// count of x_h > 0 and the sum of max(x_h, 0).
-template <int MT, int KS, int QPW>
+// source) with the shared micro-kernel; grid (row groups, seed chunks of
+// kSeedChunk), so that a few thousand rows still fill every CU.  The STATS
+// build (grid: row groups) instead takes the per-head activation statistics
+// of its rows over the 128-seed sample (dense [n_sample, D]): the count of
+// x_h > 0 and the sum of max(x_h, 0); apart, the scoring build keeps the
+// register budget of the plain score kernel.
+constexpr int kSeedChunk = 4096;
+template <int MT, int KS, int QPW, bool STATS>
 __global__ __launch_bounds__(256, 2) void dosa_seed_score(
     const DosaCtx* ctx, const uint16_t* __restrict__ q, const uint16_t* __restrict__ sk,
     const uint16_t* __restrict__ smp, int n_sample, const float* __restrict__ w,
@@ -338,12 +342,17 @@ __global__ __launch_bounds__(256, 2) void dosa_seed_score(
   constexpr int CHUNKS = 32 * CPK;
   constexpr int CPT = (CHUNKS + 255) / 256;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][32 * ROWB];
+  // this workgroup's seeds: chunk blockIdx.y of kSeedChunk
+  const int s_lo = (int)blockIdx.y * kSeedChunk;
+  const int s_n = n_seeds - s_lo < kSeedChunk ? n_seeds - s_lo : kSeedChunk;
   if (ctx->global_fallback) {  // rows take the exact path; keep the buffer defined
-    for (int i = 0; i < 4 * QPW; ++i) {
-      const int r = (int)blockIdx.x * 4 * QPW + i;
-      if (r < n_q)
-        for (int j = threadIdx.x; j < n_seeds; j += 256) seed_scores[(int64_t)r * n_seeds + j] = 0.0f;
-    }
+    if (!STATS)
+      for (int i = 0; i < 4 * QPW; ++i) {
+        const int r = (int)blockIdx.x * 4 * QPW + i;
+        if (r < n_q)
+          for (int j = threadIdx.x; j < s_n; j += 256)
+            seed_scores[(int64_t)r * n_seeds + s_lo + j] = 0.0f;
+      }
     return;
   }
   const int lane = threadIdx.x & 63, wave = wave_index();
@@ -395,8 +404,8 @@ __global__ __launch_bounds__(256, 2) void dosa_seed_score(
     }
   };
 
-  {  // activation statistics over the sample (padding keys are zero: x = 0
-     // adds nothing to either statistic)
+  if constexpr (STATS) {  // activation statistics over the sample (padding
+                         // keys are zero: x = 0 adds nothing to either statistic)
     int cnt[QPW][MT][16];
     float rs[QPW][MT][16];
 #pragma unroll
@@ -446,7 +455,8 @@ __global__ __launch_bounds__(256, 2) void dosa_seed_score(
           }
         }
   }
-  stream(sk, n_seeds, [&](int t, const unsigned char* brow) {
+  if constexpr (!STATS)
+  stream(sk + (int64_t)s_lo * D, s_n, [&](int t, const unsigned char* brow) {
     f32x16 acc[QPW][MT];
     mfma_tiles<QPW, MT, KS>(
         a, [&](int s) { return as_bf16x8(*reinterpret_cast<const u32x4*>(brow + 32 * s)); },
@@ -455,8 +465,8 @@ __global__ __launch_bounds__(256, 2) void dosa_seed_score(
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
       const float sc = head_reduce<MT>(acc[i], wv[i]);
-      if (lane < 32 && r0 + i < n_q && j < n_seeds)
-        seed_scores[(int64_t)(r0 + i) * n_seeds + j] = sc;
+      if (lane < 32 && r0 + i < n_q && j < s_n)
+        seed_scores[(int64_t)(r0 + i) * n_seeds + s_lo + j] = sc;
     }
   });
 }
@@ -1319,8 +1329,12 @@ static hipError_t run_dosa(const uint16_t* q, const uint16_t* k, const float* w,
           U16(L.sample_keys)));
   constexpr int QPW = MT == 1 ? 2 : 1;
   const int n_stat = stat_sample_size(ns);
-  SI_TRY(((dosa_seed_score<MT, KS, QPW>), dim3((n_q + 4 * QPW - 1) / (4 * QPW)), dim3(256), 0, st,
-          ctx, q, U16(L.seed_keys), U16(L.sample_keys), n_stat, w, wst, n_q, H, ns,
+  SI_TRY(((dosa_seed_score<MT, KS, QPW, true>), dim3((n_q + 4 * QPW - 1) / (4 * QPW)),
+          dim3(256), 0, st, ctx, q, U16(L.seed_keys), U16(L.sample_keys), n_stat, w, wst, n_q, H,
+          ns, F(L.seed_scores), I(L.stat_cnt), F(L.stat_sum)));
+  SI_TRY(((dosa_seed_score<MT, KS, QPW, false>),
+          dim3((n_q + 4 * QPW - 1) / (4 * QPW), (ns + kSeedChunk - 1) / kSeedChunk), dim3(256), 0,
+          st, ctx, q, U16(L.seed_keys), U16(L.sample_keys), n_stat, w, wst, n_q, H, ns,
           F(L.seed_scores), I(L.stat_cnt), F(L.stat_sum)));
   {
     TopkArgs ta;
