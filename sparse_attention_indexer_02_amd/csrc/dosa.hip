@@ -215,6 +215,7 @@ __global__ void dosa_count(const int32_t* rep_ids, int64_t n, int32_t* counts, i
 
 // Seeds: the caller's (validated) or the first n_seeds keys of [0, c) by
 // (count desc, key asc), written ascending; the seed bitmap is set.
+constexpr int kSelLdsKeys = 40960;  // common prefixes up to this many keys stage their counts in LDS
 __global__ __launch_bounds__(1024) void dosa_select_seeds(DosaCtx* ctx, const int32_t* counts,
                                                           int R, int n_seeds,
                                                           const int32_t* caller_seeds,
@@ -240,8 +241,13 @@ __global__ __launch_bounds__(1024) void dosa_select_seeds(DosaCtx* ctx, const in
     return;
   }
   // per-wave histograms of the counts (atomics contend within a wave only),
-  // then ge[v] := #{count >= v}
+  // then ge[v] := #{count >= v}.  The clamped counts (<= kMaxRep) are also
+  // kept as bytes in LDS when the prefix fits, so the passes below, where a
+  // thread walks its own run of keys, read LDS rather than strided global
+  // memory.
   __shared__ int hw[T / 64][kMaxRep + 2];
+  __shared__ uint8_t cb[kSelLdsKeys];
+  const bool staged = c <= kSelLdsKeys;
   const int wv = threadIdx.x >> 6;
   for (int v = threadIdx.x & 63; v <= R + 1; v += 64) hw[wv][v] = 0;
   __syncthreads();
@@ -249,6 +255,7 @@ __global__ __launch_bounds__(1024) void dosa_select_seeds(DosaCtx* ctx, const in
     int cnt = counts[j];
     cnt = cnt > R ? R : cnt;
     atomicAdd(&hw[wv][cnt], 1);
+    if (staged) cb[j] = (uint8_t)cnt;
   }
   __syncthreads();
   for (int v = threadIdx.x; v <= R + 1; v += T) {
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(1024) void dosa_select_seeds(DosaCtx* ctx, const in
   // output slots (the seed list is in increasing key order)
   const int per = (c + T - 1) / T;
   const int j0 = (int)threadIdx.x * per, j1 = j0 + per < c ? j0 + per : c;
-  auto cnt_of = [&](int j) { return counts[j] > R ? R : counts[j]; };
+  auto cnt_of = [&](int j) { return staged ? (int)cb[j] : (counts[j] > R ? R : counts[j]); };
   int n_eq = 0;
   for (int j = j0; j < j1; ++j) n_eq += cnt_of(j) == vstar ? 1 : 0;
   int tot;
