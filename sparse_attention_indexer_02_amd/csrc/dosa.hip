@@ -886,6 +886,7 @@ __global__ __launch_bounds__(256, 2) void dosa_bound(
 
 // Bitmap -> ascending survivor ids (one workgroup per row).
 constexpr int kCompThreads = 256;
+constexpr int kCompStage = 8192;  // ids a round stages in LDS (capacities up to this)
 __global__ __launch_bounds__(kCompThreads) void dosa_compact(
     const DosaCtx* ctx, const uint32_t* __restrict__ bitmap, int64_t words,
     const int32_t* __restrict__ vis_len, int64_t n_k, int cap, const int32_t* __restrict__ bound_cnt,
@@ -906,19 +907,48 @@ __global__ __launch_bounds__(kCompThreads) void dosa_compact(
   int64_t off;
   const int64_t v = visible_len(vis_len, nullptr, r, n_k, n_k, &off);
   const int64_t nw = over ? 0 : (v + 31) / 32;
-  const int64_t per = (nw + kCompThreads - 1) / kCompThreads;
-  const int64_t w0 = (int64_t)threadIdx.x * per;
-  int mine = 0;
-  for (int64_t i = w0; i < w0 + per && i < nw; ++i) mine += __popc(bitmap[(int64_t)r * words + i]);
-  int total;
-  int pos = block_excl_scan<kCompThreads>(mine, red, &total);
-  if (!over) {
+  const uint32_t* brow = bitmap + (int64_t)r * words;
+  int32_t* out = surv_ids + (int64_t)r * cap;
+  int total = 0;
+  if (cap <= kCompStage) {
+    // rounds of 4 kCompThreads words, thread t taking words 4t .. 4t + 3:
+    // a block scan of the per-thread counts places each id in LDS, and the
+    // round's ids leave in one coalesced pass (a round never holds more than
+    // the row's count, at most cap <= kCompStage)
+    __shared__ int32_t stage[kCompStage];
+    const int t = (int)threadIdx.x;
+    for (int64_t r0 = 0; r0 < nw; r0 += 4 * kCompThreads) {
+      const int64_t wi = r0 + 4 * t;
+      uint32_t m[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m[j] = wi + j < nw ? brow[wi + j] : 0u;
+      const int c = __popc(m[0]) + __popc(m[1]) + __popc(m[2]) + __popc(m[3]);
+      int tot;
+      int p = block_excl_scan<kCompThreads>(c, red, &tot);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        for (uint32_t mm = m[j]; mm != 0u; mm &= mm - 1u) {
+          if (p < kCompStage) stage[p] = (int32_t)((wi + j) * 32 + (__ffs(mm) - 1));
+          ++p;
+        }
+      __syncthreads();
+      for (int i = t; i < tot && i < kCompStage; i += kCompThreads)
+        if (total + i < cap) out[total + i] = stage[i];
+      total += tot;
+      __syncthreads();  // the next round's ids reuse the stage
+    }
+  } else {
+    const int64_t per = (nw + kCompThreads - 1) / kCompThreads;
+    const int64_t w0 = (int64_t)threadIdx.x * per;
+    int mine = 0;
+    for (int64_t i = w0; i < w0 + per && i < nw; ++i) mine += __popc(brow[i]);
+    int pos = block_excl_scan<kCompThreads>(mine, red, &total);
     for (int64_t i = w0; i < w0 + per && i < nw; ++i) {
-      uint32_t m = bitmap[(int64_t)r * words + i];
+      uint32_t m = brow[i];
       while (m) {
         int b = __ffs(m) - 1;
         m &= m - 1;
-        surv_ids[(int64_t)r * cap + pos++] = (int32_t)(i * 32 + b);
+        out[pos++] = (int32_t)(i * 32 + b);
       }
     }
   }
